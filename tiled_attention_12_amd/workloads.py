@@ -1,0 +1,54 @@
+"""The five reference workloads: shapes, distributions, seeds.
+
+Workload i (1-based) draws its inputs from seed 1000 + i. ``scale`` is the
+float32 value passed to the kernels; the CPU side widens that same float32.
+"""
+
+import math
+
+import numpy as np
+
+F32_SCALE_64 = float(np.float32(1.0 / math.sqrt(64)))
+F32_SCALE_128 = float(np.float32(1.0 / math.sqrt(128)))
+F32_SCALE_576 = float(np.float32(1.0 / math.sqrt(576)))
+
+WORKLOADS = {
+    "mha_tiny_f32": dict(kind="mha", dtype="f32", B=1, H=2, Sq=128, Skv=128, D=64,
+                         causal=(False,), sigma=1.0, scale=F32_SCALE_64, seed=1001),
+    "mha_prefill_bf16": dict(kind="mha", dtype="bf16", B=4, H=16, Sq=2048, Skv=2048, D=128,
+                             causal=(False, True), sigma=1.0, scale=F32_SCALE_128, seed=1002),
+    "mha_long_causal_bf16": dict(kind="mha", dtype="bf16", B=1, H=32, Sq=16384, Skv=16384,
+                                 D=128, causal=(True,), sigma=0.5, scale=F32_SCALE_128,
+                                 seed=1003),
+    "mla_decode_bf16": dict(kind="mla", B=64, H=128, kv_len=4096, sigma=0.3,
+                            scale=F32_SCALE_576, seed=1004),
+    "mla_decode_ragged_bf16": dict(kind="mla", B=128, H=128, kv_len_range=(1024, 16384),
+                                   sigma=0.3, scale=F32_SCALE_576, seed=1005),
+}
+
+
+def mha_flops(B, H, Sq, Skv, D, causal, Dv=None):
+    """FLOPs of the two contractions (Q*K^T and P*V) over visible pairs only."""
+    Dv = D if Dv is None else Dv
+    if causal:
+        pairs = int(np.clip(np.arange(Sq, dtype=np.int64) + (Skv - Sq) + 1, 0, Skv).sum())
+    else:
+        pairs = Sq * Skv
+    return 2 * B * H * pairs * (D + Dv)
+
+
+def mha_bytes(B, H, Sq, Skv, D, elem, Hkv=None, Dv=None):
+    """Algorithmic HBM bytes: Q, K, V read once, O written once, fp32 LSE written once."""
+    Hkv = H if Hkv is None else Hkv
+    Dv = D if Dv is None else Dv
+    return elem * (B * H * Sq * D + B * Hkv * Skv * (D + Dv) + B * H * Sq * Dv) + 4 * B * H * Sq
+
+
+def mla_flops(H, total_keys, Dl=512, Dr=64):
+    """FLOPs of the score products (Dl + Dr wide) and P*V (Dl wide) per key."""
+    return 2 * H * (Dl + Dr + Dl) * int(total_keys)
+
+
+def mla_bytes(B, H, total_keys, Dl=512, Dr=64):
+    """Algorithmic HBM bytes: KV and K_pe rows, Q and Q_pe read once; O (bf16) and LSE written."""
+    return 2 * (Dl + Dr) * int(total_keys) + 2 * B * H * (Dl + Dr) + 2 * B * H * Dl + 4 * B * H
