@@ -1,0 +1,132 @@
+/*
+ * tattn -- tiled fused attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libtattn.so. Every entry point is asynchronous: it validates its
+ * arguments on the host, enqueues kernels on `stream` and returns. Nothing is
+ * launched and nothing is written when validation fails. Errors raised by the
+ * device while the kernels run surface at the caller's next synchronisation
+ * on that stream. No entry point synchronises the device.
+ *
+ * Pointers named as device pointers must point to device memory (for example
+ * from hipMalloc or torch on a ROCm device); `stream` is a hipStream_t passed
+ * as void* (NULL selects the default stream of the current device). The
+ * library never frees, retains or reallocates caller memory; outputs are
+ * fully overwritten (never accumulated into). Calls are reentrant and may be
+ * issued concurrently on different streams.
+ *
+ * bf16 tensors are raw IEEE bfloat16 bit patterns (uint16 storage). All
+ * tensors are dense, row-major (last index fastest), with no padding.
+ *
+ * Source of the method: the four TileLang web pages this library is based
+ * on. "TileLang study notes" (section "FlashAttention implementation") gives
+ * the attention definition S = Q*K^T, P = softmax(S), O = P*V and the
+ * online-softmax recurrence; "TileLang programming model and FlashMLA"
+ * (sections 2.1-2.2, 3.1) gives the MLA decode kernel with its exp2 softmax
+ * and running log-sum.
+ */
+#ifndef TATTN_H
+#define TATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+#define TATTN_OK               0   /* enqueued (or nothing to do)                       */
+#define TATTN_ERR_INVALID_ARG (-1) /* null pointer, negative size, non-finite scale ... */
+#define TATTN_ERR_UNSUPPORTED (-2) /* valid request outside the supported shapes        */
+#define TATTN_ERR_ALIGN       (-3) /* a pointer misses its required alignment           */
+#define TATTN_ERR_OOM         (-4) /* device workspace could not be allocated           */
+#define TATTN_ERR_HIP         (-5) /* no usable HIP device, or a launch failed           */
+
+/*
+ * attn_fwd -- multi-head attention forward, bf16 in, fp32 accumulate.
+ *
+ * Computes, for every batch b < B, head h < H and query row i < Sq,
+ *   O[b,h,i,:]  = sum_j P_ij * V[b,h,j,:],  P_ij = exp(s_ij) / sum_j' exp(s_ij'),
+ *   LSE[b,h,i]  = ln sum_j exp(s_ij),       s_ij = scale * Q[b,h,i,:] . K[b,h,j,:],
+ * over the keys j the row may see: all j < Skv, or with causal != 0 the keys
+ * j <= i + (Skv - Sq) (the mask is aligned to the bottom-right corner; for
+ * Sq == Skv this is j <= i). This is the attention definition and the online
+ * softmax recurrence of "TileLang study notes", section "FlashAttention
+ * implementation"; LSE is the running log-sum ("logsum") of "TileLang
+ * programming model and FlashMLA", section 3.1, in natural-log units.
+ * The score matrix never reaches memory.
+ *
+ *   q   device, bf16 [B, H, Sq,  D], 16-byte aligned, read only
+ *   k   device, bf16 [B, H, Skv, D], 16-byte aligned, read only
+ *   v   device, bf16 [B, H, Skv, D], 16-byte aligned, read only
+ *   o   device, bf16 [B, H, Sq,  D], 16-byte aligned, written (RNE from fp32)
+ *   lse device, fp32 [B, H, Sq],      4-byte aligned, written
+ *   B, H, Sq >= 0 (any of them 0: nothing to do, TATTN_OK); Skv >= 0
+ *   D   head dimension: 64 or 128 (else TATTN_ERR_UNSUPPORTED)
+ *   causal 0 or 1; scale any finite float (typically 1/sqrt(D))
+ *
+ * A row that sees no key (Skv == 0, or causal rows with i + Skv - Sq < 0)
+ * gets O = 0 and LSE = -inf. q/k/v may overlap each other; o and lse must
+ * not overlap any input or each other.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Sq, int Skv, int D, int causal, float scale,
+             void* stream);
+
+/*
+ * attn_fwd_f32 -- the same operation as attn_fwd with fp32 q, k, v and o
+ * (fp32 arithmetic throughout). Same arguments, layouts, masking, edge
+ * cases and status codes; q, k, v, o are fp32 and 16-byte aligned.
+ * D is 64 or 128.
+ */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int H, int Sq, int Skv, int D, int causal, float scale,
+                 void* stream);
+
+/*
+ * mla_decode -- multi-head latent attention decode (one query position per
+ * batch), bf16 in, fp32 accumulate.
+ *
+ * "TileLang programming model and FlashMLA" (sections 2.1-2.2, 3.1): the H
+ * query heads of a batch share one KV head made of a 512-wide latent part
+ * KV and a 64-wide rotary part K_pe. For batch b, head h and key j of that
+ * batch, s_hj = scale * (Q[b,h,:] . KV[j,:] + Q_pe[b,h,:] . K_pe[j,:]);
+ * the values are the latent rows themselves, so
+ *   O[b,h,:]  = sum_j P_hj * KV[j,:],  LSE[b,h] = ln sum_j exp(s_hj).
+ *
+ * Keys of all batches are packed back to back: batch b owns rows
+ * kv_indptr[b] <= j < kv_indptr[b+1] of kv and k_pe.
+ *
+ *   q         device, bf16 [B, H, 512], 16-byte aligned
+ *   q_pe      device, bf16 [B, H, 64],  16-byte aligned
+ *   kv        device, bf16 [N, 512],    16-byte aligned, N = kv_indptr[B]
+ *   k_pe      device, bf16 [N, 64],     16-byte aligned
+ *   o         device, bf16 [B, H, 512], 16-byte aligned, written
+ *   lse       device, fp32 [B, H],      4-byte aligned, written
+ *   B >= 0 (0: nothing to do); H a multiple of 32 with 32 <= H <= 128
+ *   kv_indptr device, int32 [B+1], 4-byte aligned, read on the device only:
+ *             kv_indptr[0] >= 0 and non-decreasing; the caller guarantees
+ *             that rows up to kv_indptr[B] exist. A decreasing pair is
+ *             treated as an empty batch.
+ *   scale     any finite float (typically 1/sqrt(576))
+ *
+ * A batch with no keys gets O = 0 and LSE = -inf. Work is split along the
+ * packed key axis over the GPU's compute units; each piece writes a
+ * normalised partial output and its log-sum-exp into a device workspace
+ * that is allocated and freed in stream order on `stream`
+ * ((CUs + B) * H * 513 * 4 bytes plus the split plan), and a second kernel
+ * merges the pieces of each batch. TATTN_ERR_OOM if that workspace cannot
+ * be allocated.
+ */
+int mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe,
+               void* o, float* lse, int B, int H, const int32_t* kv_indptr,
+               float scale, void* stream);
+
+/* Static, NUL-terminated description of a status code ("unknown status"
+ * for a value that is not one of the codes above). Never returns NULL. */
+const char* tattn_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TATTN_H */

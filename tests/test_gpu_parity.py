@@ -1,0 +1,276 @@
+"""GPU parity of the HIP path against the CPU float64 oracle (needs gfx950).
+
+Every case draws seeded inputs, runs the library through the C ABI (via the
+ctypes binding), and compares with the oracle on the same stored values:
+element by element at sizes the oracle finishes quickly (several tiles and
+a ragged tail), and on sampled rows / (batch, head) pairs at the full
+workload sizes in the configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.helpers import assert_bf16_parity, assert_f32_parity, parity_stats, to_dev, to_np
+from tiled_attention_12_amd import inputs
+from tiled_attention_12_amd.workloads import WORKLOADS
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ta(lib_path):
+    import tiled_attention_12_amd as ta
+    return ta
+
+
+def _vals(x, names):
+    return [inputs.stored_values(x[n]) for n in names]
+
+
+def _run_mha(ta, dev, x, causal, scale, fp32=False):
+    q, k, v = (to_dev(x[n], dev) for n in "qkv")
+    fn = ta.attn_fwd_f32 if fp32 else ta.attn_fwd
+    o, lse = fn(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(lse)
+
+
+# ------------------------------------------------------------------ fp32 path
+
+def test_tiny_fp32_workload(ta, dev):
+    w = WORKLOADS["mha_tiny_f32"]
+    x = inputs.mha_inputs(w["B"], w["H"], w["Sq"], w["Skv"], w["D"], seed=w["seed"], dtype="f32")
+    o, lse = _run_mha(ta, dev, x, False, w["scale"], fp32=True)
+    ro, rl = oracle.attention(x["q"], x["k"], x["v"], w["scale"])
+    st = assert_f32_parity(o, lse, ro, rl, "tiny fp32")
+    print("tiny fp32", st)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("sq,skv", [(1, 1), (33, 70), (130, 130), (64, 200), (200, 64)])
+def test_fp32_shapes(ta, dev, D, causal, sq, skv):
+    x = inputs.mha_inputs(2, 2, sq, skv, D, seed=100 + sq + skv + D, dtype="f32")
+    scale = float(np.float32(D ** -0.5))
+    o, lse = _run_mha(ta, dev, x, causal, scale, fp32=True)
+    ro, rl = oracle.attention(x["q"], x["k"], x["v"], scale, causal=causal)
+    assert_f32_parity(o, lse, ro, rl, f"fp32 D={D} causal={causal} {sq}x{skv}")
+
+
+# ------------------------------------------------------------------ bf16 prefill
+
+SHAPES = [(1, 1), (7, 7), (63, 63), (64, 64), (65, 65), (127, 129), (129, 127), (200, 257),
+          (256, 256), (300, 300), (5, 300), (300, 5), (130, 1000)]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("sq,skv", SHAPES)
+def test_bf16_shapes(ta, dev, D, causal, sq, skv):
+    x = inputs.mha_inputs(2, 3, sq, skv, D, seed=7 * sq + skv + D + int(causal))
+    scale = float(np.float32(D ** -0.5))
+    o, lse = _run_mha(ta, dev, x, causal, scale)
+    ro, rl = oracle.attention(*_vals(x, "qkv"), scale, causal=causal)
+    assert_bf16_parity(o, lse, ro, rl, f"bf16 D={D} causal={causal} {sq}x{skv}")
+
+
+def test_bf16_empty_keys_and_fully_masked_rows(ta, dev):
+    x = inputs.mha_inputs(1, 2, 40, 0, 128, seed=3)
+    q = to_dev(x["q"], dev)
+    kv = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=dev)
+    o, lse = ta.attn_fwd(q, kv, kv)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+    # Sq > Skv causal: the first Sq - Skv rows see nothing
+    x = inputs.mha_inputs(1, 2, 150, 20, 64, seed=4)
+    o, lse = _run_mha(ta, dev, x, True, 0.125)
+    ro, rl = oracle.attention(*_vals(x, "qkv"), 0.125, causal=True)
+    assert np.all(o[:, :, :130] == 0) and np.all(np.isneginf(lse[:, :, :130]))
+    assert_bf16_parity(o, lse, ro, rl, "Sq > Skv causal")
+
+
+def test_bf16_single_and_identical_keys(ta, dev):
+    x = inputs.mha_inputs(1, 2, 100, 1, 128, seed=5)
+    o, lse = _run_mha(ta, dev, x, False, 0.1)
+    v = inputs.stored_values(x["v"]).astype(np.float64)
+    assert np.array_equal(o, np.broadcast_to(v, o.shape))
+    ro, rl = oracle.attention(*_vals(x, "qkv"), 0.1)
+    assert np.abs(lse - rl).max() <= 1e-3
+    x = inputs.mha_inputs(1, 2, 70, 150, 64, seed=6)
+    x["k"][:] = x["k"][:, :, :1]
+    o, lse = _run_mha(ta, dev, x, False, 0.1)
+    v = inputs.stored_values(x["v"]).astype(np.float64)
+    assert np.abs(o - v.mean(axis=2, keepdims=True)).max() <= 1e-2
+    ro, rl = oracle.attention(*_vals(x, "qkv"), 0.1)
+    assert np.abs(lse - rl).max() <= 1e-3
+
+
+def test_bf16_causal_row0_and_future_keys(ta, dev):
+    x = inputs.mha_inputs(2, 2, 333, 333, 128, seed=11)
+    o1, l1 = _run_mha(ta, dev, x, True, 0.09)
+    v = inputs.stored_values(x["v"]).astype(np.float64)
+    assert np.array_equal(o1[:, :, 0], v[:, :, 0])
+    y = {n: x[n].copy() for n in "qkv"}
+    y["k"][:, :, 200:] = inputs.f32_to_bf16_bits(np.float32(2.0) * inputs.stored_values(y["k"][:, :, 200:]))
+    y["v"][:, :, 200:] = inputs.f32_to_bf16_bits(np.float32(-3.0) * inputs.stored_values(y["v"][:, :, 200:]))
+    o2, l2 = _run_mha(ta, dev, y, True, 0.09)
+    assert np.array_equal(o1[:, :, :200], o2[:, :, :200])
+    assert np.array_equal(l1[:, :, :200], l2[:, :, :200])
+
+
+def test_bf16_row_shift_invariance(ta, dev):
+    # a key column of ones plus a per-row query entry adds a constant to each score row
+    x = inputs.mha_inputs(1, 1, 96, 160, 64, seed=12)
+    q = inputs.stored_values(x["q"]).copy()
+    k = inputs.stored_values(x["k"]).copy()
+    k[..., 0] = 1.0
+    q[..., 0] = 0.0
+    base = {"q": inputs.f32_to_bf16_bits(q), "k": inputs.f32_to_bf16_bits(k), "v": x["v"]}
+    shift = q.copy()
+    shift[..., 0] = np.linspace(-8, 8, 96, dtype=np.float32).reshape(1, 1, 96)
+    moved = dict(base, q=inputs.f32_to_bf16_bits(shift))
+    o1, l1 = _run_mha(ta, dev, base, False, 0.125)
+    o2, l2 = _run_mha(ta, dev, moved, False, 0.125)
+    c = 0.125 * inputs.stored_values(moved["q"])[..., 0].astype(np.float64)
+    assert np.abs(o1 - o2).max() <= 1e-2
+    assert np.abs((l2 - l1) - c).max() <= 2e-3
+
+
+def test_bf16_deterministic(ta, dev):
+    x = inputs.mha_inputs(2, 4, 300, 300, 128, seed=13)
+    a = _run_mha(ta, dev, x, True, 0.088)
+    b = _run_mha(ta, dev, x, True, 0.088)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _sampled_mha(ta, dev, name, causal, n_bh, rows):
+    w = WORKLOADS[name]
+    x = inputs.mha_inputs(w["B"], w["H"], w["Sq"], w["Skv"], w["D"], seed=w["seed"], sigma=w["sigma"])
+    o, lse = _run_mha(ta, dev, x, causal, w["scale"])
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(0)
+    pairs = [(int(rng.integers(w["B"])), int(rng.integers(w["H"]))) for _ in range(n_bh)]
+    pairs[0], pairs[-1] = (0, 0), (w["B"] - 1, w["H"] - 1)
+    stats = []
+    for b, h in pairs:
+        sl = lambda n: inputs.stored_values(x[n][b:b + 1, h:h + 1])
+        ro, rl = oracle.attention(sl("q"), sl("k"), sl("v"), w["scale"], causal=causal, rows=rows)
+        st = assert_bf16_parity(o[b:b + 1, h:h + 1, rows], lse[b:b + 1, h:h + 1, rows], ro, rl,
+                                f"{name} causal={causal} b={b} h={h}")
+        stats.append(st)
+    print(name, causal, max(s["max_o"] for s in stats), max(s["max_lse"] for s in stats))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_workload_sampled(ta, dev, causal):
+    S = 2048
+    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 129, 1023, 1024, S - 129, S - 128, S - 1],
+                                     np.random.default_rng(1).integers(0, S, 52)]))
+    _sampled_mha(ta, dev, "mha_prefill_bf16", causal, 6, rows)
+
+
+def test_long_causal_workload_sampled(ta, dev):
+    S = 16384
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 8191, 8192, S - 129, S - 128, S - 1],
+                                     np.random.default_rng(2).integers(0, S, 30)]))
+    _sampled_mha(ta, dev, "mha_long_causal_bf16", True, 4, rows)
+
+
+# ------------------------------------------------------------------ MLA decode
+
+def _run_mla(ta, dev, m, scale):
+    args = [to_dev(m[n], dev) for n in ("q", "q_pe", "kv", "k_pe")]
+    o, lse = ta.mla_decode(*args, to_dev(m["indptr"], dev), scale)
+    torch.cuda.synchronize()
+    return to_np(o), to_np(lse)
+
+
+def _mla_vals(m):
+    return [inputs.stored_values(m[n]) for n in ("q", "q_pe", "kv", "k_pe")]
+
+
+@pytest.mark.parametrize("H", [32, 64, 128])
+@pytest.mark.parametrize("lens", [[1], [31, 32, 33], [0, 5, 0, 64, 1], [500, 1, 77], [0, 0]])
+def test_mla_small(ta, dev, H, lens):
+    B = len(lens)
+    rng = np.random.default_rng(sum(lens) + H)
+    m = inputs.mla_inputs(B, H, seed=int(rng.integers(1 << 30)), kv_len=1)
+    # rebuild with the requested lengths (same generator recipe, explicit lengths)
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n = int(indptr[-1])
+    g = np.random.default_rng(int(rng.integers(1 << 30)))
+    m["kv"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 512), dtype=np.float32) * np.float32(0.3))
+    m["k_pe"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 64), dtype=np.float32) * np.float32(0.3))
+    m["indptr"] = indptr
+    if n == 0:
+        m["kv"] = np.zeros((1, 512), np.uint16)
+        m["k_pe"] = np.zeros((1, 64), np.uint16)
+    scale = float(np.float32(576 ** -0.5))
+    o, lse = _run_mla(ta, dev, m, scale)
+    ro, rl = oracle.mla_decode(*_mla_vals(m), indptr, scale)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
+    assert_bf16_parity(o, lse, ro, rl, f"mla H={H} lens={lens}")
+
+
+def test_mla_ragged_batch_equals_standalone(ta, dev):
+    lens = [700, 3000, 129, 4097]
+    m = inputs.mla_inputs(len(lens), 128, seed=21, kv_len=1)
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    g = np.random.default_rng(22)
+    n = int(indptr[-1])
+    m["kv"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 512), dtype=np.float32) * np.float32(0.3))
+    m["k_pe"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 64), dtype=np.float32) * np.float32(0.3))
+    m["indptr"] = indptr
+    scale = float(np.float32(576 ** -0.5))
+    o, lse = _run_mla(ta, dev, m, scale)
+    b = 3
+    one = {"q": m["q"][b:b + 1], "q_pe": m["q_pe"][b:b + 1], "kv": m["kv"][indptr[b]:indptr[b + 1]],
+           "k_pe": m["k_pe"][indptr[b]:indptr[b + 1]], "indptr": np.array([0, lens[b]], np.int32)}
+    o1, l1 = _run_mla(ta, dev, one, scale)
+    assert np.abs(o[b] - o1[0]).max() <= 1e-2 and np.abs(lse[b] - l1[0]).max() <= 1e-3
+    ro, rl = oracle.mla_decode(*_mla_vals(m), indptr, scale)
+    assert_bf16_parity(o, lse, ro, rl, "mla ragged 4")
+
+
+def test_mla_deterministic(ta, dev):
+    m = inputs.mla_inputs(8, 128, seed=23, kv_len_range=(1, 3000))
+    scale = float(np.float32(576 ** -0.5))
+    a = _run_mla(ta, dev, m, scale)
+    b = _run_mla(ta, dev, m, scale)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def _sampled_mla(ta, dev, name, n_pairs):
+    w = WORKLOADS[name]
+    kw = {"kv_len": w["kv_len"]} if "kv_len" in w else {"kv_len_range": w["kv_len_range"]}
+    m = inputs.mla_inputs(w["B"], w["H"], seed=w["seed"], sigma=w["sigma"], **kw)
+    o, lse = _run_mla(ta, dev, m, w["scale"])
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(3)
+    lens = m["lens"]
+    pairs = [(int(rng.integers(w["B"])), int(rng.integers(w["H"]))) for _ in range(n_pairs)]
+    pairs += [(int(np.argmax(lens)), 0), (int(np.argmin(lens)), w["H"] - 1), (w["B"] - 1, 5)]
+    ro, rl = oracle.mla_decode_rows(*_mla_vals(m), m["indptr"], w["scale"], pairs)
+    idx_b = [p[0] for p in pairs]
+    idx_h = [p[1] for p in pairs]
+    st = assert_bf16_parity(o[idx_b, idx_h], lse[idx_b, idx_h], ro, rl, name)
+    print(name, st)
+
+
+def test_mla_decode_workload_sampled(ta, dev):
+    _sampled_mla(ta, dev, "mla_decode_bf16", 48)
+
+
+def test_mla_ragged_workload_sampled(ta, dev):
+    _sampled_mla(ta, dev, "mla_decode_ragged_bf16", 48)

@@ -1,0 +1,152 @@
+"""ctypes binding of libtattn.so: argument marshalling only.
+
+Every function here checks dtypes, devices, shapes and contiguity of torch
+tensors, allocates outputs with torch, and passes raw device pointers plus
+the current HIP stream to the C ABI. All arithmetic runs in the library's
+gfx950 kernels; if the library is missing, loading this module fails.
+"""
+
+import ctypes
+import math
+import os
+
+from ._build import library_path
+
+TATTN_OK = 0
+TATTN_ERR_INVALID_ARG = -1
+TATTN_ERR_UNSUPPORTED = -2
+TATTN_ERR_ALIGN = -3
+TATTN_ERR_OOM = -4
+TATTN_ERR_HIP = -5
+
+EXPORTED = ("attn_fwd", "attn_fwd_f32", "mla_decode", "tattn_status_str")
+
+
+class TattnError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} (status {status})")
+
+
+def _load():
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is not built; run `python -m tiled_attention_12_amd.build` "
+            "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    mha = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, vp]
+    lib.attn_fwd.argtypes = mha
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd_f32.argtypes = mha
+    lib.attn_fwd_f32.restype = i32
+    lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, f32, vp]
+    lib.mla_decode.restype = i32
+    lib.tattn_status_str.argtypes = [i32]
+    lib.tattn_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+_LIB = _load()
+
+
+def lib():
+    """The loaded ctypes library (raw C ABI)."""
+    return _LIB
+
+
+def status_str(status):
+    return _LIB.tattn_status_str(int(status)).decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_ptr(device, stream):
+    torch = _torch()
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() > 0 else ctypes.c_void_p(0)
+
+
+def _check_dev(name, t, dtype, device):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a ROCm device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _mha(fn_name, q, k, v, causal, scale, out, lse, stream, dtype):
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    Skv = k.shape[2]
+    if tuple(k.shape) != (B, H, Skv, D) or tuple(v.shape) != (B, H, Skv, D):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    _check_dev("out", out, dtype, dev)
+    _check_dev("lse", lse, torch.float32, dev)
+    if tuple(out.shape) != (B, H, Sq, D) or tuple(lse.shape) != (B, H, Sq):
+        raise ValueError("out/lse have the wrong shape")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = getattr(_LIB, fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, Skv, D,
+                                int(bool(causal)), ctypes.c_float(scale), _stream_ptr(dev, stream))
+    if rc != TATTN_OK:
+        raise TattnError(rc, fn_name)
+    return out, lse
+
+
+def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+    """bf16 multi-head attention forward: returns (O bf16 [B,H,Sq,D], LSE fp32 [B,H,Sq])."""
+    return _mha("attn_fwd", q, k, v, causal, scale, out, lse, stream, _torch().bfloat16)
+
+
+def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
+    """fp32 multi-head attention forward: returns (O fp32 [B,H,Sq,D], LSE fp32 [B,H,Sq])."""
+    return _mha("attn_fwd_f32", q, k, v, causal, scale, out, lse, stream, _torch().float32)
+
+
+def mla_decode(q, q_pe, kv, k_pe, kv_indptr, scale, out=None, lse=None, stream=None):
+    """MLA decode: q [B,H,512], q_pe [B,H,64], kv [N,512], k_pe [N,64] (bf16),
+    kv_indptr int32 [B+1] on the device. Returns (O bf16 [B,H,512], LSE fp32 [B,H])."""
+    torch = _torch()
+    if q.dim() != 3 or q_pe.dim() != 3 or kv.dim() != 2 or k_pe.dim() != 2:
+        raise ValueError("q [B,H,512], q_pe [B,H,64], kv [N,512], k_pe [N,64]")
+    B, H, Dl = q.shape
+    N = kv.shape[0]
+    if Dl != 512 or tuple(q_pe.shape) != (B, H, 64) or kv.shape[1] != 512 or tuple(k_pe.shape) != (N, 64):
+        raise ValueError("MLA widths must be 512 (latent) and 64 (rotary)")
+    dev = q.device
+    for n, t in (("q", q), ("q_pe", q_pe), ("kv", kv), ("k_pe", k_pe)):
+        _check_dev(n, t, torch.bfloat16, dev)
+    _check_dev("kv_indptr", kv_indptr, torch.int32, dev)
+    if tuple(kv_indptr.shape) != (B + 1,):
+        raise ValueError("kv_indptr must have B + 1 entries")
+    if out is None:
+        out = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.bfloat16, dev)
+    _check_dev("lse", lse, torch.float32, dev)
+    rc = _LIB.mla_decode(_ptr(q), _ptr(q_pe), _ptr(kv), _ptr(k_pe), _ptr(out), _ptr(lse), B, H,
+                         _ptr(kv_indptr), ctypes.c_float(float(scale)), _stream_ptr(dev, stream))
+    if rc != TATTN_OK:
+        raise TattnError(rc, "mla_decode")
+    return out, lse

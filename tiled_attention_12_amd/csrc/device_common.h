@@ -1,0 +1,191 @@
+// Device helpers shared by the gfx950 attention kernels.
+//
+// Lane layouts used throughout (wave64, checked on the hardware):
+//  * v_mfma_f32_32x32x16_bf16: A (32x16) lane l holds row l%32, k = 8*(l/32)+j
+//    for j = 0..7; B (16x32) lane l holds column l%32, k = 8*(l/32)+j;
+//    C/D (32x32 fp32) lane l holds column l%32, rows 8*(i/4) + 4*(l/32) + i%4
+//    for i = 0..15.
+//  * ds_read_b64_tr_b16: inside each group of 16 lanes, lane i receives, as
+//    its element r (r = 0..3), element i%4 of the 8-byte block addressed by
+//    lane 4*r + i/4 of the same group.
+//  * global_load_lds_dwordx4: lane l's 16 bytes land at LDS base + 16*l, the
+//    base being wave-uniform.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <utility>
+
+namespace tattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// Compile-time loop: f(std::integral_constant<int, i>{}) for i = 0..N-1, so
+// the body can use i as a constant expression (template arguments, asm
+// immediates).
+template <int... Is, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, Is...>, F&& f) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Position of 16-byte chunk `c` of row `r` inside a tile whose rows hold
+// `CPR` chunks. The XOR on the low chunk bits makes the two LDS read
+// patterns conflict-free: 16 consecutive rows at one chunk (MFMA operand
+// reads along a row) and 4 aligned rows x 4 aligned chunks (the transposing
+// reads of the value operand).
+template <int CPR>
+__device__ __forceinline__ int swz(int r, int c) {
+  if constexpr (CPR >= 16) {
+    return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else {
+    static_assert(CPR == 8, "rows of 8 or >= 16 chunks");
+    return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+}
+
+// 16-byte direct global -> LDS load. `lds_base` must be wave-uniform; lane l
+// writes lds_base + 16*l.
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)gptr, (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 lds_read128(const void* p) {
+  return *(const __attribute__((address_space(3))) u32x4*)((__attribute__((address_space(3))) const char*)(uintptr_t)p);
+}
+
+// ds_read_b64_tr_b16 issued through inline asm. The compiler does not see it
+// as an LDS access, so it neither counts it for lgkmcnt nor makes it wait for
+// in-flight global->LDS loads into other buffers; the caller waits with
+// wait_lds_tied() before using the result. `byte_off` is the instruction's
+// immediate offset.
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16_async(uint32_t lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF));
+  return r;
+}
+
+// s_waitcnt lgkmcnt(0) that the listed values depend on, so no use of them
+// can be scheduled above the wait.
+__device__ __forceinline__ void wait_lds_tied(u32x2& a, u32x2& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void wait_lds_tied(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+template <int N>
+__device__ __forceinline__ void wait_lds_tied(u32x2 (&r)[N]) {
+  static_assert(N % 4 == 0, "groups of 4");
+  if constexpr (N == 4) {
+    wait_lds_tied(r[0], r[1], r[2], r[3]);
+  } else {
+    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]),
+                 "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
+    if constexpr (N > 8) {
+      static_assert(N == 16, "up to 16 values");
+      asm volatile("" : "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]),
+                   "+v"(r[13]), "+v"(r[14]), "+v"(r[15]));
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
+}
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (0 << 8));
+}
+
+// Workgroup barrier that orders LDS traffic only: callers wait for the
+// counters they need first. The asm memory clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void barrier() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// v_permlane32_swap with both operands = x returns, in every lane l, the pair
+// {x(l), x(l ^ 32)} (in lane-dependent order), so these reductions across the
+// two wave halves give identical bits in lanes l and l ^ 32.
+__device__ __forceinline__ float max_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x *= alpha for an MFMA accumulator that lives in AGPRs, element by element
+// through one temporary VGPR (VALU cannot read AGPRs directly), so a rare
+// rescale of a large accumulator never needs a block of VGPRs.
+__device__ __forceinline__ void scale_acc16(f32x16& x, float alpha) {
+  float e[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) e[i] = x[i];
+  float t;
+#define TATTN_SCALE4(i0, i1, i2, i3)                                                        \
+  asm volatile(                                                                            \
+      "v_accvgpr_read_b32 %4, %0\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %0, %4\n\t" \
+      "v_accvgpr_read_b32 %4, %1\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %1, %4\n\t" \
+      "v_accvgpr_read_b32 %4, %2\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %2, %4\n\t" \
+      "v_accvgpr_read_b32 %4, %3\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %3, %4"       \
+      : "+a"(e[i0]), "+a"(e[i1]), "+a"(e[i2]), "+a"(e[i3]), "=&v"(t)                           \
+      : "v"(alpha))
+  TATTN_SCALE4(0, 1, 2, 3);
+  TATTN_SCALE4(4, 5, 6, 7);
+  TATTN_SCALE4(8, 9, 10, 11);
+  TATTN_SCALE4(12, 13, 14, 15);
+#undef TATTN_SCALE4
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = e[i];
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Round two floats to bf16 (nearest-even) and pack them, lo in bits 15:0.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ bf16x8 cat_tr(u32x2 a, u32x2 b) {
+  u32x4 r = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+}  // namespace tattn

@@ -1,0 +1,27 @@
+// Internal launchers called by the C ABI layer (tattn.cpp). Each enqueues
+// its kernels on `stream` and returns the launch status; arguments are
+// already validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tattn {
+
+hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int H, int Sq, int Skv, int D, bool causal, float scale,
+                               hipStream_t stream);
+
+hipError_t launch_mha_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                              int B, int H, int Sq, int Skv, int D, bool causal, float scale,
+                              hipStream_t stream);
+
+// Bytes of device workspace mla_decode needs for B batches and H heads when
+// split over `n_split` workgroups.
+size_t mla_workspace_bytes(int B, int H, int n_split);
+
+hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe,
+                             void* o, float* lse, int B, int H, const int32_t* kv_indptr,
+                             float scale, int n_split, void* workspace, hipStream_t stream);
+
+}  // namespace tattn

@@ -1,0 +1,424 @@
+// MLA decode forward (one query position per batch), bf16 in, fp32 accumulate.
+//
+// Method: the FlashMLA decode kernel of "TileLang programming model and
+// FlashMLA" -- the query heads of a batch share one KV head; each KV tile is
+// staged in fast memory once, scores are the sum of the latent product
+// (Q * KV^T) and the rotary product (Q_pe * K_pe^T) (section 2.2), the
+// softmax is max-subtracted base-2 with the scale folded in and a running
+// log-sum (section 3.1), and the tile loop is software pipelined (section
+// 2.2). The values are the latent rows themselves, so one LDS tile serves
+// as both keys and values.
+//
+// Three kernels:
+//  1. plan:    tile_ptr[b] = number of 32-key tiles in batches before b.
+//  2. split:   one persistent workgroup per compute unit takes an equal,
+//              contiguous slice of the packed tile range (a slice may span
+//              batches) and, for each batch it touches, writes the
+//              normalised partial output O_s and its log-sum-exp lse_s into
+//              slot (workgroup + batch), which is unique per piece.
+//  3. combine: for every (batch, head), lse = ln sum_s exp(lse_s) and
+//              O = sum_s exp(lse_s - lse) * O_s, rounded to bf16. This merge
+//              is exact: each O_s is normalised by its own exp(lse_s).
+//
+// gfx950 mapping of the split kernel: 4 waves x 32 heads (H = 128); wave w
+// holds Q^T of its heads in registers (B operand, 36 k-steps of 16) and the
+// O^T accumulator (16 blocks of 32 latent columns) in accumulation
+// registers. Per 32-key tile: S^T = KV * Q^T + K_pe * Q_pe^T with the tile
+// read from LDS as the A operand (v_mfma_f32_32x32x16_bf16), then the
+// online softmax in lane-per-head form, then O^T += KV^T * P^T with KV^T read
+// by ds_read_b64_tr_b16 from the same tile. Tiles arrive by
+// global_load_lds_dwordx4 through a 4-stage LDS ring.
+#include "device_common.h"
+#include "launch.h"
+
+namespace tattn {
+
+constexpr int kDl = 512;     // latent width
+constexpr int kDr = 64;      // rotary width
+constexpr int kBK = 32;      // keys per tile
+constexpr int kTileL = kBK * kDl * 2;
+constexpr int kTileR = kBK * kDr * 2;
+constexpr int kStage = kTileL + kTileR;
+
+struct MlaArgs {
+  const uint16_t* q;
+  const uint16_t* qpe;
+  const uint16_t* kv;
+  const uint16_t* kpe;
+  uint16_t* o;
+  float* lse;
+  const int32_t* indptr;
+  int B, H;
+  float c;          // scale * log2(e)
+  int* tile_ptr;    // [B + 1]
+  float* part_lse;  // [(P + B) * H]
+  float* part_o;    // [(P + B) * H * 512]
+};
+
+__device__ __forceinline__ int batch_tiles(const int32_t* indptr, int b) {
+  const int len = indptr[b + 1] - indptr[b];
+  return len > 0 ? (len + kBK - 1) / kBK : 0;
+}
+
+// Workgroup w of P takes global tiles [start(w), start(w + 1)).
+__device__ __forceinline__ int split_start(int w, int T, int P) {
+  return (int)(((long long)w * T) / P);
+}
+
+// The workgroup whose slice holds global tile g (0 <= g < T).
+__device__ __forceinline__ int split_owner(int g, int T, int P) {
+  int w = (int)(((long long)g * P) / T);
+  while (w + 1 < P && split_start(w + 1, T, P) <= g) ++w;
+  while (w > 0 && split_start(w, T, P) > g) --w;
+  return w;
+}
+
+__global__ __launch_bounds__(1024) void mla_plan_kernel(const int32_t* indptr, int B, int* tile_ptr) {
+  __shared__ int sums[1024];
+  const int t = threadIdx.x;
+  const int per = (B + 1023) / 1024;
+  const int b0 = min(B, t * per), b1 = min(B, b0 + per);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) local += batch_tiles(indptr, b);
+  sums[t] = local;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = t >= off ? sums[t - off] : 0;
+    __syncthreads();
+    sums[t] += add;
+    __syncthreads();
+  }
+  int run = t > 0 ? sums[t - 1] : 0;
+  for (int b = b0; b < b1; ++b) {
+    tile_ptr[b] = run;
+    run += batch_tiles(indptr, b);
+  }
+  if (t == 1023) tile_ptr[B] = sums[1023];
+}
+
+template <int NW, int NSTAGE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_split_kernel(MlaArgs a) {
+  constexpr int KS = (kDl + kDr) / 16;          // 36 k-steps of the score product
+  constexpr int KSL = kDl / 16;                 // 32 of them on the latent part
+  constexpr int DB = kDl / 32;                  // 16 output blocks
+  constexpr int LAT_LOADS = kBK / NW;           // one 1 KB latent row per wave load
+  constexpr int PE_LOADS = kBK * (kDr / 8) / (64 * NW);
+  constexpr int LPT = LAT_LOADS + PE_LOADS;     // loads per wave per tile
+  static_assert(kBK * (kDr / 8) % (64 * NW) == 0, "rotary tile must split into wave loads");
+  static_assert((NSTAGE - 2) * LPT < 64, "vmcnt range");
+  constexpr float TAU = 8.0f;
+
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hi = lane >> 5, col = lane & 31;
+  const int H = a.H;
+  const int head = wave * 32 + col;
+  const float c = a.c;
+
+  // Lane-dependent parts of the LDS addresses. The swizzle only permutes the
+  // low 4 chunk bits, so every read is one of these bases plus a constant
+  // (higher chunk bits, row half, stage) that fits the instruction offset.
+  uint32_t kbase[8], pbase[4], tbase[2][4];
+  {
+    const int sg = ((col & 3) << 2) | ((col >> 2) & 3);
+#pragma unroll
+    for (int r = 0; r < 8; ++r) kbase[r] = col * 1024 + 16 * ((2 * r + hi) ^ sg);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pbase[r] = kTileL + col * 128 + 16 * swz<8>(col, 2 * r + hi);
+    const int gq = (lane >> 4) & 1, s16 = lane & 15;
+    const int x = 2 * gq + ((s16 & 3) >> 1), boff = 8 * (s16 & 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int rr = 8 * e + 4 * hi + (s16 >> 2);
+      const int sr = ((rr & 3) << 2) | ((rr >> 2) & 3);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) tbase[e][r] = rr * 1024 + 16 * ((4 * r + x) ^ sr) + boff;
+    }
+  }
+
+  const int w = blockIdx.x, P = gridDim.x;
+  const int T = a.tile_ptr[a.B];
+  int g = split_start(w, T, P);
+  const int gend = split_start(w + 1, T, P);
+  if (g >= gend) return;
+
+  int b;
+  {
+    int lo = 0, up = a.B;  // tile_ptr[lo] <= g < tile_ptr[up]
+    while (up - lo > 1) {
+      const int mid = (lo + up) >> 1;
+      if (a.tile_ptr[mid] <= g) lo = mid; else up = mid;
+    }
+    b = lo;
+  }
+
+  while (true) {
+    const int tb = a.tile_ptr[b];
+    const int seg_end = min(gend, a.tile_ptr[b + 1]);
+    const int t0 = g - tb, nt = seg_end - g;
+    const int kv_lo = a.indptr[b];
+    const int kv_hi = a.indptr[b + 1];
+
+    // all waves are done with the LDS ring of the previous piece
+    wait_lgkmcnt0();
+    barrier();
+
+    // Tile i of this piece -> LDS stage i % NSTAGE. Every latent load of a
+    // wave covers one key row (uniform, so its base address is scalar); the
+    // lane picks the global chunk lane ^ sigma(row). Rotary loads cover 8 rows.
+    auto issue = [&](int i) {
+      char* sl = smem + (i % NSTAGE) * kStage;
+      const int key0 = kv_lo + (t0 + i) * kBK;
+#pragma unroll
+      for (int n = 0; n < LAT_LOADS; ++n) {
+        const int row = n * NW + wave;
+        const int gr = min(key0 + row, kv_hi - 1);
+        const char* rowp = (const char*)(a.kv + (size_t)gr * kDl);
+        const uint32_t voff = (uint32_t)swz<64>(row, lane) * 16u;
+        load_lds16(rowp + voff, sl + row * 1024);
+      }
+#pragma unroll
+      for (int n = 0; n < PE_LOADS; ++n) {
+        const int slot = (n * NW + wave) * 64 + lane;
+        const int row = slot >> 3;
+        const int rc = min(row, kv_hi - 1 - key0);
+        const char* tilep = (const char*)(a.kpe + (size_t)key0 * kDr);
+        const uint32_t voff = (uint32_t)(rc * kDr * 2 + swz<8>(row, slot & 7) * 16);
+        load_lds16(tilep + voff, sl + kTileL + (n * NW + wave) * 1024);
+      }
+    };
+
+    // Q^T fragments of this wave's heads
+    bf16x8 qf[KS];
+    {
+      const uint16_t* qr = a.q + ((size_t)b * H + head) * kDl + hi * 8;
+      const uint16_t* pr = a.qpe + ((size_t)b * H + head) * kDr + hi * 8;
+#pragma unroll
+      for (int ks = 0; ks < KSL; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(qr + ks * 16));
+#pragma unroll
+      for (int ks = KSL; ks < KS; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(pr + (ks - KSL) * 16));
+    }
+
+#pragma unroll
+    for (int i = 0; i < NSTAGE - 1; ++i)
+      if (i < nt) issue(i);
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
+
+    for (int i = 0; i < nt; ++i) {
+      const int ahead = min(NSTAGE - 2, nt - 1 - i);
+      if constexpr (NSTAGE == 4) {
+        if (ahead >= 2) wait_vmcnt<2 * LPT>();
+        else if (ahead == 1) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+      } else {
+        if (ahead >= 1) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+      }
+      barrier();
+      if (i + NSTAGE - 1 < nt) issue(i + NSTAGE - 1);
+
+      const char* sl = smem + (i % NSTAGE) * kStage;
+      const int nvalid = min(kBK, kv_hi - (kv_lo + (t0 + i) * kBK));
+
+      // ---- S^T = KV * Q^T + K_pe * Q_pe^T
+      const uint32_t sbase = lds_addr(sl);
+      f32x16 s = f32x16{};
+      {
+        constexpr int G = 4;
+        static_for<KS / G>([&](auto K0) {
+          constexpr int k0 = decltype(K0)::value * G;
+          bf16x8 kf[G];
+          static_for<G>([&](auto U) {
+            constexpr int ks = k0 + decltype(U)::value;
+            const uint32_t addr = ks < KSL ? sbase + kbase[ks & 7] + 256 * (ks >> 3) : sbase + pbase[ks - KSL];
+            kf[U] = as_bf16x8(lds_read128((const void*)(uintptr_t)addr));
+          });
+          static_for<G>([&](auto U) { s = mfma32(kf[U], qf[k0 + decltype(U)::value], s); });
+          __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+        });
+      }
+
+      if (nvalid < kBK) {
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2)
+          if (8 * (i2 >> 2) + 4 * hi + (i2 & 3) >= nvalid) s[i2] = -INFINITY;
+      }
+
+      // ---- online softmax (lane = head)
+      bf16x8 pf[2];
+      {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, s[i2]);
+        mx = max_halves(mx) * c;
+        const bool raise = mx - m > TAU;
+        if (__builtin_amdgcn_ballot_w64(raise)) {
+          const float alpha = raise ? fast_exp2(m - mx) : 1.f;
+          m = raise ? mx : m;
+          lsum *= alpha;
+          static_for<DB>([&](auto DBc) { scale_acc16(oacc[DBc], alpha); });
+        }
+        const float mc = m == -INFINITY ? 0.f : m;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            p[j] = fast_exp2(fmaf(s[half * 8 + j], c, -mc));
+            lsum += p[j];
+          }
+          u32x4 x = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                     pack_bf16x2(p[6], p[7])};
+          pf[half] = as_bf16x8(x);
+        }
+      }
+
+      // ---- O^T += KV^T * P^T (KV^T by transposing reads of the latent tile);
+      // the reads of block db+1 are in flight while block db's MFMAs run.
+      {
+        uint32_t vb[2][4];
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) vb[e][r] = sbase + tbase[e][r];
+        auto vread = [&](auto DBc, u32x2 (&r)[4]) {
+          constexpr int db = decltype(DBc)::value;
+          r[0] = lds_read_tr16_async<(db >> 2) * 256>(vb[0][db & 3]);
+          r[1] = lds_read_tr16_async<(db >> 2) * 256>(vb[1][db & 3]);
+          r[2] = lds_read_tr16_async<16384 + (db >> 2) * 256>(vb[0][db & 3]);
+          r[3] = lds_read_tr16_async<16384 + (db >> 2) * 256>(vb[1][db & 3]);
+        };
+        u32x2 vr[2][4];
+        vread(std::integral_constant<int, 0>{}, vr[0]);
+        wait_lds_tied(vr[0]);
+        static_for<DB>([&](auto DBc) {
+          constexpr int db = decltype(DBc)::value;
+          if constexpr (db + 1 < DB) vread(std::integral_constant<int, db + 1>{}, vr[(db + 1) & 1]);
+          oacc[db] = mfma32(cat_tr(vr[db & 1][0], vr[db & 1][1]), pf[0], oacc[db]);
+          oacc[db] = mfma32(cat_tr(vr[db & 1][2], vr[db & 1][3]), pf[1], oacc[db]);
+          if constexpr (db + 1 < DB) wait_lds_tied(vr[(db + 1) & 1]);
+        });
+      }
+    }
+
+    // ---- normalised partial of this piece -> slot (workgroup + batch)
+    {
+      const float l = sum_halves(lsum);
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const size_t slot = (size_t)w + b;
+      float* po = a.part_o + (slot * H + head) * kDl;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + 8 * g4 + 4 * hi;
+          f32x4 v = {oacc[db][g4 * 4] * inv, oacc[db][g4 * 4 + 1] * inv, oacc[db][g4 * 4 + 2] * inv,
+                     oacc[db][g4 * 4 + 3] * inv};
+          *(f32x4*)(po + d) = v;
+        }
+      if (hi == 0) a.part_lse[slot * H + head] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+    }
+
+    g = seg_end;
+    if (g >= gend) break;
+    do { ++b; } while (a.tile_ptr[b + 1] <= g);
+  }
+}
+
+// One workgroup of 128 threads per (batch, head); thread t owns latent
+// columns 4t .. 4t+3.
+__global__ __launch_bounds__(128) void mla_combine_kernel(MlaArgs a, int P) {
+  const int bh = blockIdx.x;
+  const int b = bh / a.H, h = bh - b * a.H;
+  const int t = threadIdx.x;
+  const int T = a.tile_ptr[a.B];
+  const int g0 = a.tile_ptr[b], g1 = a.tile_ptr[b + 1];
+  uint16_t* orow = a.o + (size_t)bh * kDl + 4 * t;
+  if (g0 >= g1) {
+    *(u32x2*)orow = u32x2{0u, 0u};
+    if (t == 0) a.lse[bh] = -INFINITY;
+    return;
+  }
+  const int w0 = split_owner(g0, T, P), w1 = split_owner(g1 - 1, T, P);
+  // Workgroups between the two owners with an empty slice (possible when
+  // there are fewer tiles than workgroups) wrote nothing and are skipped.
+  float mx = -INFINITY;
+  for (int w = w0; w <= w1; ++w) {
+    if (split_start(w, T, P) == split_start(w + 1, T, P)) continue;
+    mx = fmaxf(mx, a.part_lse[((size_t)w + b) * a.H + h]);
+  }
+  float tot = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int w = w0; w <= w1; ++w) {
+    if (split_start(w, T, P) == split_start(w + 1, T, P)) continue;
+    const size_t slot = (size_t)w + b;
+    const float ls = a.part_lse[slot * a.H + h];
+    const float wt = ls == -INFINITY ? 0.f : __expf(ls - mx);
+    tot += wt;
+    acc += wt * *(const f32x4*)(a.part_o + (slot * a.H + h) * kDl + 4 * t);
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  *(u32x2*)orow = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (t == 0) a.lse[bh] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t mla_workspace_bytes(int B, int H, int n_split) {
+  const size_t slots = (size_t)n_split + B;
+  return align256((size_t)(B + 1) * 4) + align256(slots * H * 4) + slots * H * kDl * 4;
+}
+
+template <int NW, int NSTAGE>
+static hipError_t launch_split(const MlaArgs& a, int n_split, hipStream_t stream) {
+  constexpr size_t lds = (size_t)NSTAGE * kStage;
+  auto kern = mla_split_kernel<NW, NSTAGE>;
+  static const hipError_t attr_err =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr_err != hipSuccess) return attr_err;
+  hipLaunchKernelGGL(kern, dim3(n_split), dim3(NW * 64), lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe,
+                             void* o, float* lse, int B, int H, const int32_t* kv_indptr,
+                             float scale, int n_split, void* workspace, hipStream_t stream) {
+  MlaArgs a{};
+  a.q = (const uint16_t*)q;
+  a.qpe = (const uint16_t*)q_pe;
+  a.kv = (const uint16_t*)kv;
+  a.kpe = (const uint16_t*)k_pe;
+  a.o = (uint16_t*)o;
+  a.lse = lse;
+  a.indptr = kv_indptr;
+  a.B = B;
+  a.H = H;
+  a.c = scale * kLog2e;
+  char* ws = (char*)workspace;
+  const size_t slots = (size_t)n_split + B;
+  a.tile_ptr = (int*)ws;
+  a.part_lse = (float*)(ws + align256((size_t)(B + 1) * 4));
+  a.part_o = (float*)(ws + align256((size_t)(B + 1) * 4) + align256(slots * H * 4));
+
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, kv_indptr, B, a.tile_ptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (H) {
+    case 128: e = launch_split<4, 4>(a, n_split, stream); break;
+    case 64: e = launch_split<2, 4>(a, n_split, stream); break;
+    default: e = launch_split<1, 3>(a, n_split, stream); break;
+  }
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(B * H), dim3(128), 0, stream, a, n_split);
+  return hipGetLastError();
+}
+
+}  // namespace tattn

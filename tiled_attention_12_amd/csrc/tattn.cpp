@@ -1,0 +1,141 @@
+// C ABI of libtattn.so: argument validation, dispatch to the gfx950
+// launchers, stream-ordered workspace for the split decode. See
+// include/tattn.h for the contract of every entry point.
+#include "tattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <mutex>
+
+#include "launch.h"
+
+#define TATTN_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxSeq = 1 << 30;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int status_of(hipError_t e) {
+  if (e == hipSuccess) return TATTN_OK;
+  if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return TATTN_ERR_OOM;
+  return TATTN_ERR_HIP;
+}
+
+// Compute-unit count of the current device (cached per device ordinal).
+int current_device_cus(int* cus) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TATTN_ERR_HIP;
+  static std::mutex mu;
+  static int cache[256] = {0};
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 256 && cache[dev] > 0) {
+    *cus = cache[dev];
+    return TATTN_OK;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return TATTN_ERR_HIP;
+  if (dev < 256) cache[dev] = n;
+  *cus = n;
+  return TATTN_OK;
+}
+
+int have_device() {
+  int dev = -1;
+  return (hipGetDevice(&dev) == hipSuccess && dev >= 0) ? TATTN_OK : TATTN_ERR_HIP;
+}
+
+// Shared validation of the two MHA entry points. Returns TATTN_OK with
+// *nothing = true when there is no work.
+int check_mha(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
+              int Sq, int Skv, int D, int causal, float scale, bool* nothing) {
+  *nothing = false;
+  if (B < 0 || H < 0 || Sq < 0 || Skv < 0) return TATTN_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return TATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return TATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return TATTN_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || Sq == 0) {
+    *nothing = true;
+    return TATTN_OK;
+  }
+  if (!q || !o || !lse || (Skv > 0 && (!k || !v))) return TATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(lse, 4) || (Skv > 0 && (!aligned(k, 16) || !aligned(v, 16))))
+    return TATTN_ERR_ALIGN;
+  if (Sq > kMaxSeq || Skv > kMaxSeq) return TATTN_ERR_UNSUPPORTED;
+  const long long n_bh = (long long)B * H;
+  if (n_bh > INT_MAX || n_bh * ((Sq + 31) / 32) > INT_MAX) return TATTN_ERR_UNSUPPORTED;
+  return TATTN_OK;
+}
+
+}  // namespace
+
+TATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Sq,
+                       int Skv, int D, int causal, float scale, void* stream) {
+  bool nothing = false;
+  int st = check_mha(q, k, v, o, lse, B, H, Sq, Skv, D, causal, scale, &nothing);
+  if (st != TATTN_OK || nothing) return st;
+  if ((st = have_device()) != TATTN_OK) return st;
+  return status_of(tattn::launch_mha_fwd_bf16(q, k, v, o, lse, B, H, Sq, Skv, D, causal != 0, scale,
+                                              (hipStream_t)stream));
+}
+
+TATTN_API int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
+                           int Sq, int Skv, int D, int causal, float scale, void* stream) {
+  bool nothing = false;
+  int st = check_mha(q, k, v, o, lse, B, H, Sq, Skv, D, causal, scale, &nothing);
+  if (st != TATTN_OK || nothing) return st;
+  if ((Sq + 63) / 64 > 65535) return TATTN_ERR_UNSUPPORTED;
+  if ((st = have_device()) != TATTN_OK) return st;
+  return status_of(tattn::launch_mha_fwd_f32(q, k, v, o, lse, B, H, Sq, Skv, D, causal != 0, scale,
+                                             (hipStream_t)stream));
+}
+
+TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe, void* o, float* lse,
+                         int B, int H, const int32_t* kv_indptr, float scale, void* stream) {
+  if (B < 0 || H < 0) return TATTN_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return TATTN_ERR_INVALID_ARG;
+  if (B == 0) return TATTN_OK;
+  if (H != 32 && H != 64 && H != 128) return TATTN_ERR_UNSUPPORTED;
+  if (!q || !q_pe || !kv || !k_pe || !o || !lse || !kv_indptr) return TATTN_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(q_pe, 16) || !aligned(kv, 16) || !aligned(k_pe, 16) || !aligned(o, 16) ||
+      !aligned(lse, 4) || !aligned(kv_indptr, 4))
+    return TATTN_ERR_ALIGN;
+  if ((long long)B * H > INT_MAX || B > (1 << 24)) return TATTN_ERR_UNSUPPORTED;
+
+  int cus = 0;
+  int st = current_device_cus(&cus);
+  if (st != TATTN_OK) return st;
+  const size_t bytes = tattn::mla_workspace_bytes(B, H, cus);
+  if (const char* cap = std::getenv("TATTN_WS_LIMIT_BYTES")) {
+    if (bytes > (size_t)std::strtoull(cap, nullptr, 10)) return TATTN_ERR_OOM;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, s);
+  if (e != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return TATTN_ERR_OOM;
+  }
+  e = tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, cus, ws, s);
+  const hipError_t ef = hipFreeAsync(ws, s);
+  if (e != hipSuccess) return status_of(e);
+  return status_of(ef);
+}
+
+TATTN_API const char* tattn_status_str(int status) {
+  switch (status) {
+    case TATTN_OK: return "ok";
+    case TATTN_ERR_INVALID_ARG: return "invalid argument";
+    case TATTN_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+    case TATTN_ERR_ALIGN: return "pointer misaligned";
+    case TATTN_ERR_OOM: return "device workspace allocation failed";
+    case TATTN_ERR_HIP: return "HIP runtime error or no usable device";
+    default: return "unknown status";
+  }
+}
