@@ -1,0 +1,251 @@
+"""Benchmark of the tiled attention forward on one MI355X.
+
+One step = one pass of the prefill hot path over the headline workload
+(bf16 MHA B=4, H=16, Sq=Skv=2048, D=128), run once non-causal and once
+causal. The long causal prefill (B=1, H=32, S=16384) and the two MLA decode
+workloads are measured in the same run and reported under "workloads".
+Inputs are seeded synthetic draws, resident in HBM before timing; each
+workload rotates three input copies so consecutive launches read cold data.
+
+Prints one JSON line (see --help for the flags).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+N_COPIES = 3
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _to_dev(arr, dev):
+    import torch
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+
+def _copies(arrs, dev):
+    """N_COPIES device copies of each stored input array."""
+    import torch
+    out = []
+    for c in range(N_COPIES):
+        out.append({k: (_to_dev(v, dev) if c == 0 else None) for k, v in arrs.items()})
+    for c in range(1, N_COPIES):
+        for k in arrs:
+            out[c][k] = out[0][k].clone()
+    torch.cuda.synchronize()
+    return out
+
+
+def _time_launches(fn, sets, warmup, reps):
+    """Average duration (ms) of fn(set) over reps launches, with HIP events on
+    the stream the kernels are launched on (torch's current stream)."""
+    import torch
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
+        fn(sets[i % len(sets)])
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    d = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
+    return float(np.mean(d)), float(np.median(d)), float(np.min(d))
+
+
+def _mha_workload(ta, dev, name):
+    from tiled_attention_12_amd import inputs
+    from tiled_attention_12_amd.workloads import WORKLOADS
+    w = WORKLOADS[name]
+    x = inputs.mha_inputs(w["B"], w["H"], w["Sq"], w["Skv"], w["D"], seed=w["seed"], sigma=w["sigma"])
+    return w, _copies(x, dev)
+
+
+def _mla_workload(ta, dev, name):
+    from tiled_attention_12_amd import inputs
+    from tiled_attention_12_amd.workloads import WORKLOADS
+    w = WORKLOADS[name]
+    kw = {"kv_len": w["kv_len"]} if "kv_len" in w else {"kv_len_range": w["kv_len_range"]}
+    m = inputs.mla_inputs(w["B"], w["H"], seed=w["seed"], sigma=w["sigma"], **kw)
+    total = int(m["indptr"][-1])
+    sets = _copies({k: m[k] for k in ("q", "q_pe", "kv", "k_pe", "indptr")}, dev)
+    return w, sets, total
+
+
+def _cpu_baseline(budget_s=12.0):
+    """The CPU oracle, as it stands, on a bounded sample of the headline
+    workload: whole (batch, head) slices, non-causal and causal alternately,
+    until about budget_s seconds of CPU work. Reported in TFLOP/s."""
+    import oracle
+    from tiled_attention_12_amd import inputs
+    from tiled_attention_12_amd.workloads import WORKLOADS, mha_flops
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    w = WORKLOADS["mha_prefill_bf16"]
+    S, D = w["Sq"], w["D"]
+    x = inputs.mha_inputs(1, 8, S, S, D, seed=w["seed"], sigma=w["sigma"])
+    q, k, v = (inputs.stored_values(x[n]) for n in "qkv")
+    flops = 0
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < budget_s and n < 4096:
+        h = n % 8
+        causal = bool(n % 2)
+        oracle.attention(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], w["scale"], causal=causal)
+        flops += mha_flops(1, 1, S, S, D, causal)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} whole (batch, head) slices of the S=2048, D=128 bf16 prefill "
+                      f"(alternating non-causal/causal), {dt:.1f} s of float64 numpy on the host"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--skip-secondary", action="store_true",
+                    help="only the headline prefill workload (for profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(the kernels run on one GPU's share; see the design notes on sharding).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_attention_12_amd as ta
+    from tiled_attention_12_amd.workloads import mha_bytes, mha_flops, mla_bytes, mla_flops
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---------------------------------------------------------------- headline prefill
+    _log("bench: preparing the headline prefill workload")
+    w, sets = _mha_workload(ta, dev, "mha_prefill_bf16")
+    B, H, S, D = w["B"], w["H"], w["Sq"], w["D"]
+    outs = [ta.attn_fwd(s["q"], s["k"], s["v"], causal=False, scale=w["scale"]) for s in sets[:1]]
+    o_buf, l_buf = outs[0]
+    f_nc, f_c = mha_flops(B, H, S, S, D, False), mha_flops(B, H, S, S, D, True)
+    nbytes = mha_bytes(B, H, S, S, D, 2)
+
+    def step(i):
+        s = sets[i % N_COPIES]
+        ta.attn_fwd(s["q"], s["k"], s["v"], causal=False, scale=w["scale"], out=o_buf, lse=l_buf)
+        ta.attn_fwd(s["q"], s["k"], s["v"], causal=True, scale=w["scale"], out=o_buf, lse=l_buf)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # per-launch events: non-causal launch j is bracketed by ev[2j], ev[2j+1]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    ev[0].record()
+    for i in range(args.steps):
+        s = sets[i % N_COPIES]
+        ta.attn_fwd(s["q"], s["k"], s["v"], causal=False, scale=w["scale"], out=o_buf, lse=l_buf)
+        ev[2 * i + 1].record()
+        ta.attn_fwd(s["q"], s["k"], s["v"], causal=True, scale=w["scale"], out=o_buf, lse=l_buf)
+        ev[2 * i + 2].record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    d_nc = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
+    d_c = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)]
+    total_ms = ev[0].elapsed_time(ev[-1])
+    ms_step = total_ms / args.steps
+    value = (f_nc + f_c) / (ms_step * 1e-3) / 1e12
+    nc_ms, c_ms = float(np.mean(d_nc)), float(np.mean(d_c))
+    _log(f"bench: prefill non-causal {nc_ms * 1e3:.1f} us, causal {c_ms * 1e3:.1f} us, "
+         f"step {ms_step * 1e3:.1f} us, wall {t_wall:.3f} s")
+
+    workloads = {
+        "mha_prefill_bf16_noncausal": {
+            "ms": nc_ms, "tflops": f_nc / (nc_ms * 1e-3) / 1e12,
+            "frac_mfma_peak": f_nc / (nc_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+        "mha_prefill_bf16_causal": {
+            "ms": c_ms, "tflops": f_c / (c_ms * 1e-3) / 1e12,
+            "frac_mfma_peak": f_c / (c_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS},
+    }
+    del sets
+
+    if not args.skip_secondary:
+        _log("bench: long causal prefill")
+        w3, sets3 = _mha_workload(ta, dev, "mha_long_causal_bf16")
+        o3, l3 = ta.attn_fwd(sets3[0]["q"], sets3[0]["k"], sets3[0]["v"], causal=True, scale=w3["scale"])
+        mean3, med3, min3 = _time_launches(
+            lambda s: ta.attn_fwd(s["q"], s["k"], s["v"], causal=True, scale=w3["scale"], out=o3, lse=l3),
+            sets3, 2, 10)
+        f3 = mha_flops(w3["B"], w3["H"], w3["Sq"], w3["Skv"], w3["D"], True)
+        workloads["mha_long_causal_bf16"] = {"ms": mean3, "ms_median": med3, "ms_min": min3,
+                                             "tflops": f3 / (mean3 * 1e-3) / 1e12,
+                                             "frac_mfma_peak": f3 / (mean3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        del sets3, o3, l3
+
+        for name in ("mla_decode_bf16", "mla_decode_ragged_bf16"):
+            _log(f"bench: {name}")
+            wm, setsm, total = _mla_workload(ta, dev, name)
+            s0 = setsm[0]
+            om, lm = ta.mla_decode(s0["q"], s0["q_pe"], s0["kv"], s0["k_pe"], s0["indptr"], wm["scale"])
+            mean_m, med_m, min_m = _time_launches(
+                lambda s: ta.mla_decode(s["q"], s["q_pe"], s["kv"], s["k_pe"], s["indptr"], wm["scale"],
+                                        out=om, lse=lm), setsm, 5, 30)
+            fl = mla_flops(wm["H"], total)
+            by = mla_bytes(wm["B"], wm["H"], total)
+            t_star = max(by / (PEAK_HBM_GBS * 1e9), fl / (PEAK_BF16_TFLOPS * 1e12))
+            workloads[name] = {"ms": mean_m, "ms_median": med_m, "ms_min": min_m, "total_keys": total,
+                               "kv_gbs": 1152 * total / (mean_m * 1e-3) / 1e9,
+                               "alg_gbs": by / (mean_m * 1e-3) / 1e9,
+                               "tflops": fl / (mean_m * 1e-3) / 1e12,
+                               "frac_roofline": t_star / (mean_m * 1e-3)}
+            del setsm, om, lm
+
+    achieved = f_nc / (nc_ms * 1e-3) / 1e12
+    line = {
+        "metric": "prefill attn TFLOP/s & MLA-decode KV GB/s, % of MI355X roofline",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mha_prefill_bf16: B=4 H=16 Sq=Skv=2048 D=128, non-causal + causal per step",
+                   "global_batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "mha_fwd_bf16_kernel<128,4,1,64,false> (non-causal)",
+                     "alg_flops_per_launch": f_nc, "alg_bytes_per_launch": nbytes},
+        "workloads": workloads,
+    }
+    if not args.no_cpu_baseline:
+        _log("bench: CPU oracle baseline")
+        line["cpu_baseline"] = _cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
