@@ -118,6 +118,24 @@ def _cpu_baseline(budget_s=12.0):
                       f"(alternating non-causal/causal), {dt:.1f} s of float64 numpy on the host"}
 
 
+def _profile_only(args, ta, dev):
+    """Run args.steps launches of one workload (after args.warmup) and print its mean time."""
+    import torch
+    name = args.only
+    if name.startswith("mha"):
+        causal = name != "mha_prefill_bf16"
+        w, sets = _mha_workload(ta, dev, name.replace("_causal", "") if name == "mha_prefill_bf16_causal" else name)
+        o, l = ta.attn_fwd(sets[0]["q"], sets[0]["k"], sets[0]["v"], causal=causal, scale=w["scale"])
+        fn = lambda s: ta.attn_fwd(s["q"], s["k"], s["v"], causal=causal, scale=w["scale"], out=o, lse=l)
+    else:
+        w, sets, _ = _mla_workload(ta, dev, name)
+        s0 = sets[0]
+        o, l = ta.mla_decode(s0["q"], s0["q_pe"], s0["kv"], s0["k_pe"], s0["indptr"], w["scale"])
+        fn = lambda s: ta.mla_decode(s["q"], s["q_pe"], s["kv"], s["k_pe"], s["indptr"], w["scale"], out=o, lse=l)
+    mean, med, mn = _time_launches(fn, sets, args.warmup, args.steps)
+    print(json.dumps({"only": name, "ms_mean": mean, "ms_median": med, "ms_min": mn}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +144,12 @@ def main():
     ap.add_argument("--skip-secondary", action="store_true",
                     help="only the headline prefill workload (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["mha_prefill_bf16", "mha_prefill_bf16_causal", "mha_long_causal_bf16",
+                                       "mla_decode_bf16", "mla_decode_ragged_bf16"],
+                    help="profiling mode: run --steps launches of one workload, print its timing only")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="profiling mode: first run one device-to-device copy of this many MiB "
+                         "(reference for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -138,6 +162,18 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.only:
+        _profile_only(args, ta, dev)
+        return
 
     # ---------------------------------------------------------------- headline prefill
     _log("bench: preparing the headline prefill workload")

@@ -6,4 +6,5 @@ LIB_NAME = "libtattn.so"
 
 
 def library_path():
-    return os.path.join(PKG_DIR, LIB_NAME)
+    """The in-tree libtattn.so, or the file named by TATTN_LIBRARY if set."""
+    return os.environ.get("TATTN_LIBRARY") or os.path.join(PKG_DIR, LIB_NAME)

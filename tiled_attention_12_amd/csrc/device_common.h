@@ -69,6 +69,26 @@ __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
   __builtin_amdgcn_global_load_lds((gbl_void_t*)gptr, (lds_void_t*)lds_base, 16, 0, 0);
 }
 
+// The same load issued through inline asm (M0 <- LDS base, then the load).
+// The compiler does not see this write to LDS, so its LDS reads (including
+// the transposing-read builtin) are not made to wait for it; callers order
+// LDS reuse with wait_vmcnt() and barrier(). M0 is written here and by no
+// compiler-generated code in the kernels that use this (checked in their
+// assembly), so the clobber of the reserved register is safe there.
+__device__ __forceinline__ void load_lds16_asm(const void* gptr, uint32_t lds_base_uniform) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_base_uniform) : "memory", "m0");
+}
+
+// ds_read_b64_tr_b16 through the compiler builtin (it tracks lgkmcnt and can
+// place the result directly in an MFMA operand tuple).
+template <int OFF>
+__device__ __forceinline__ u32x2 lds_read_tr16(uint32_t lds_addr) {
+  const auto r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(uintptr_t)(lds_addr + OFF));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 __device__ __forceinline__ u32x4 lds_read128(const void* p) {
   return *(const __attribute__((address_space(3))) u32x4*)((__attribute__((address_space(3))) const char*)(uintptr_t)p);
 }

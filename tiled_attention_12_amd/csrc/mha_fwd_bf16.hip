@@ -29,6 +29,8 @@
 //  * Workgroup -> tile order: the hardware hands workgroup i to XCD i % 8;
 //    all query tiles of a (batch, head) are sent to one XCD so its K/V stays
 //    in that XCD's L2, and causal launches run the longest tiles first.
+#include <cstdlib>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -47,16 +49,21 @@ struct MhaArgs {
   int remap;  // n_bh % 8 == 0: XCD-grouped order
 };
 
-template <int D, int NW, int QB, int BC, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void mha_fwd_bf16_kernel(MhaArgs a) {
-  constexpr int BR = NW * QB * 32;
-  constexpr int CPR = D / 8;   // 16-byte chunks per row
-  constexpr int KS = D / 16;   // MFMA k-steps of Q*K^T
-  constexpr int DB = D / 32;   // 32-wide blocks of the head dimension
-  constexpr int KB = BC / 32;  // 32-key blocks per tile
-  constexpr int TILE = BC * D * 2;
+template <int D, int NW, int BC, int NSTAGE, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void mha_fwd_bf16_kernel(MhaArgs a) {
+  constexpr int BR = NW * 32;      // query rows per workgroup (32 per wave)
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  constexpr int RS = D * 2;        // row stride in bytes
+  constexpr int KS = D / 16;       // MFMA k-steps of Q*K^T
+  constexpr int DB = D / 32;       // 32-wide blocks of the head dimension
+  constexpr int KB = BC / 32;      // 32-key blocks per tile
+  constexpr int TILE = BC * RS;    // bytes of one K or V tile
+  constexpr int VREG = NSTAGE * TILE;  // V tiles follow the NSTAGE K tiles
   constexpr int LOADS = BC * CPR / (64 * NW);
+  constexpr int LPT = 2 * LOADS;   // loads per wave per tile (K and V)
   static_assert(BC * CPR % (64 * NW) == 0, "tile must split into whole wave loads");
+  static_assert(NSTAGE * TILE <= 65536, "LDS offsets must fit the 16-bit instruction offset");
+  static_assert(NSTAGE == 3, "three LDS stages: the lagging wave group reads tile t-1 after barrier t");
   constexpr float TAU = 8.0f;
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -83,10 +90,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
   const int Sq = a.Sq, Skv = a.Skv;
   const int q0 = qt * BR;
-  const int wrow0 = q0 + wave * QB * 32;
+  const int wrow0 = q0 + wave * 32;
   const uint16_t* qp = a.q + (size_t)bh * Sq * D;
-  const uint16_t* kp = a.k + (size_t)bh * Skv * D;
-  const uint16_t* vp = a.v + (size_t)bh * Skv * D;
+  const char* kp = (const char*)(a.k + (size_t)bh * Skv * D);
+  const char* vp = (const char*)(a.v + (size_t)bh * Skv * D);
   const float c = a.c;
 
   int kv_end = Skv;
@@ -95,174 +102,226 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
     kv_end = max(0, min(Skv, last + Skv - Sq + 1));
   }
   const int nt = (kv_end + BC - 1) / BC;
+  // last key this wave's rows can see (causal); tiles past it are skipped
+  const int wave_kv_last = CAUSAL ? min(wrow0 + 31, Sq - 1) + Skv - Sq : Skv - 1;
 
-  auto issue = [&](int t, int stage) {
-    char* kl = smem + stage * 2 * TILE;
-    char* vl = kl + TILE;
+  // Lane-dependent LDS address parts. The XOR swizzle touches only the low
+  // 4 chunk bits and depends only on the low 4 row bits, so the key block,
+  // row half, K/V choice and stage are immediate offsets.
+  const uint32_t smem0 = lds_addr(smem);
+  uint32_t kbase[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kbase[ks] = smem0 + col * RS + 16 * swz<CPR>(col, 2 * ks + hi);
+  uint32_t vbase[2][DB];
+  {
+    const int gq = (lane >> 4) & 1, s16 = lane & 15;
+    const int x = 2 * gq + ((s16 & 3) >> 1), boff = 8 * (s16 & 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int rr = 8 * e + 4 * hi + (s16 >> 2);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) vbase[e][db] = smem0 + VREG + rr * RS + 16 * swz<CPR>(rr, db * 4 + x) + boff;
+    }
+  }
+
+  // Tile t -> stage ST: wave loads n cover chunk slots (n*NW + wave)*64 + lane.
+  auto issue = [&](int t, auto STc) {
+    constexpr int ST = decltype(STc)::value;
+    const int lim = Skv - 1 - t * BC;  // >= 0: tile t has a visible key
+    const char* kt = kp + (size_t)t * BC * RS;
+    const char* vt = vp + (size_t)t * BC * RS;
 #pragma unroll
     for (int n = 0; n < LOADS; ++n) {
       const int slot = (n * NW + wave) * 64 + lane;
       const int row = slot / CPR;
-      const int chunk = swz<CPR>(row, slot % CPR);
-      int gr = t * BC + row;
-      gr = gr < Skv ? gr : Skv - 1;
-      const size_t off = (size_t)gr * D + chunk * 8;
-      load_lds16(kp + off, kl + (n * NW + wave) * 1024);
-      load_lds16(vp + off, vl + (n * NW + wave) * 1024);
+      const uint32_t off = (uint32_t)(min(row, lim) * RS + 16 * swz<CPR>(row, slot % CPR));
+      const uint32_t dst = smem0 + ST * TILE + (n * NW + wave) * 1024;
+      load_lds16_asm(kt + off, dst);
+      load_lds16_asm(vt + off, dst + VREG);
     }
   };
 
-  if (nt > 0) issue(0, 0);
+  if (nt > 0) issue(0, std::integral_constant<int, 0>{});
 
   // Q^T fragments (B operand), loaded once.
-  bf16x8 qf[QB][KS];
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = wrow0 + qb * 32 + col;
+  bf16x8 qf[KS];
+  {
+    const int row = wrow0 + col;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       u32x4 x = {0, 0, 0, 0};
       if (row < Sq) x = *(const u32x4*)(qp + (size_t)row * D + ks * 16 + hi * 8);
-      qf[qb][ks] = as_bf16x8(x);
+      qf[ks] = as_bf16x8(x);
     }
   }
 
-  f32x16 oacc[DB][QB];
-  float m[QB], lsum[QB];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m[qb] = -INFINITY;
-    lsum[qb] = 0.f;
-#pragma unroll
-    for (int db = 0; db < DB; ++db) oacc[db][qb] = f32x16{};
-  }
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+  float m = -INFINITY, lsum = 0.f;
 
-  for (int t = 0; t < nt; ++t) {
-    const int st = t & 1;
+  // ---- the three phases of one tile (stage ST):
+  //   M1: S^T = K*Q^T (MFMA), V: masks + online softmax (VALU), M2: O^T += V^T*P^T (MFMA)
+  auto m1 = [&](auto STc, f32x16 (&s)[KB]) {
+    constexpr int ST = decltype(STc)::value;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+    // k-steps in groups of 2; inside a group the key blocks alternate, so
+    // consecutive MFMAs never depend on each other
+    static_for<KS / 2>([&](auto Gc) {
+      constexpr int g = decltype(Gc)::value;
+      bf16x8 kf[2][KB];
+      static_for<2>([&](auto Uc) {
+        static_for<KB>([&](auto KBc) {
+          kf[Uc][KBc] = as_bf16x8(lds_read128(
+              (const void*)(uintptr_t)(kbase[2 * g + Uc] + ST * TILE + decltype(KBc)::value * 32 * RS)));
+        });
+      });
+      static_for<2>([&](auto Uc) {
+        static_for<KB>([&](auto KBc) { s[KBc] = mfma32(kf[Uc][KBc], qf[2 * g + Uc], s[KBc]); });
+      });
+    });
+  };
+
+  auto vphase = [&](int t, f32x16 (&s)[KB], bf16x8 (&pf)[KB][2], auto MASKEDc) {
+    const int kv0 = t * BC;
+    if constexpr (decltype(MASKEDc)::value) {
+      const int lim = CAUSAL ? min(Skv - 1, wrow0 + col + Skv - Sq) : Skv - 1;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kv0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3) > lim) s[kb][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = max_halves(mx) * c;
+    const bool raise = mx - m > TAU;  // false when mx == -inf
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+      const float alpha = raise ? fast_exp2(m - mx) : 1.f;
+      m = raise ? mx : m;
+      lsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+    }
+    const float mc = m == -INFINITY ? 0.f : m;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = fast_exp2(fmaf(s[kb][half * 8 + j], c, -mc));
+          lsum += p[j];
+        }
+        u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                   pack_bf16x2(p[6], p[7])};
+        pf[kb][half] = as_bf16x8(w);
+      }
+  };
+
+  auto m2 = [&](auto STc, const bf16x8 (&pf)[KB][2]) {
+    constexpr int ST = decltype(STc)::value;
+    // for each 16-key slice: read the V^T fragments of all d-blocks, then one
+    // MFMA per d-block (independent accumulators back to back)
+    static_for<KB * 2>([&](auto SC) {
+      constexpr int kb = decltype(SC)::value / 2, half = decltype(SC)::value % 2;
+      constexpr int off = ST * TILE + kb * 32 * RS + half * 16 * RS;
+      bf16x8 vf[DB];
+      static_for<DB>([&](auto DBc) {
+        const u32x2 r0 = lds_read_tr16<off>(vbase[0][DBc]);
+        const u32x2 r1 = lds_read_tr16<off>(vbase[1][DBc]);
+        vf[DBc] = cat_tr(r0, r1);
+      });
+      static_for<DB>([&](auto DBc) { oacc[DBc] = mfma32(vf[DBc], pf[kb][half], oacc[DBc]); });
+    });
+  };
+
+  // Two wave groups share each SIMD: group 0 (waves 0..NW/2-1) runs
+  // M1(t) V(t) M2(t) after barrier t; group 1 runs V(t-1) M2(t-1) M1(t).
+  // Each group's VALU phase then overlaps the other group's MFMA phases.
+  // Tile t-1 stays readable until barrier t+1 because the ring has three
+  // stages and the refill issued at barrier t targets stage (t+1) % 3.
+  const bool lag = wave >= NW / 2;
+  f32x16 s_cur[KB];   // scores of the tile in flight (group 1: of tile t-1 across the barrier)
+
+  // One tile step of a group; LAG is a compile-time copy per group so the
+  // two groups' loops are allocated independently.
+  auto tile = [&](int t, auto STc, auto LAGc, bool& pending) {
+    constexpr int ST = decltype(STc)::value;
+    constexpr int SP = (ST + NSTAGE - 1) % NSTAGE;  // stage of tile t-1
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     barrier();
-    if (t + 1 < nt) issue(t + 1, st ^ 1);
-    const char* kl = smem + st * 2 * TILE;
-    const char* vl = kl + TILE;
-
-    // ---- S^T = K * Q^T (all K fragments of a key block are read before its MFMAs)
-    f32x16 s[KB][QB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const int row = kb * 32 + col;
-      bf16x8 kf[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kf[ks] = as_bf16x8(lds_read128(kl + (row * CPR + swz<CPR>(row, ks * 2 + hi)) * 16));
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[kb][qb] = mfma32(kf[ks], qf[qb][ks], s[kb][qb]);
-      // keep the KS operand reads of this key block ahead of its MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, KS * QB, 0);
+    if (t + 1 < nt) issue(t + 1, std::integral_constant<int, (ST + 1) % NSTAGE>{});
+    if constexpr (!decltype(LAGc)::value) {
+      bf16x8 pf[KB][2];
+      m1(STc, s_cur);
+      vphase(t, s_cur, pf, std::false_type{});
+      m2(STc, pf);
+    } else {
+      if (pending) {
+        bf16x8 pf[KB][2];
+        vphase(t - 1, s_cur, pf, std::false_type{});
+        m2(std::integral_constant<int, SP>{}, pf);
+      }
+      pending = true;
+      m1(STc, s_cur);
     }
+  };
 
-    // ---- masks (tail keys, causal diagonal)
-    const int kv0 = t * BC;
-    const bool need_mask = (kv0 + BC > Skv) || (CAUSAL && kv0 + BC - 1 > wrow0 + Skv - Sq);
-    if (need_mask) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int lim = CAUSAL ? min(Skv - 1, wrow0 + qb * 32 + col + Skv - Sq) : Skv - 1;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = kv0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (j > lim) s[kb][qb][i] = -INFINITY;
-          }
+  // Tiles [0, t_plain) need no mask for any wave of the workgroup; they run
+  // unrolled over the LDS stages with the two groups offset. The rest
+  // (causal diagonal, ragged tail) run in step, masked, after group 1 has
+  // finished its pending tile.
+  int t_plain = Skv / BC;
+  if (CAUSAL) t_plain = min(t_plain, max(0, (q0 + Skv - Sq + 1) / BC));
+  t_plain = min(t_plain, nt);
+  const int t_main = t_plain - t_plain % NSTAGE;
+  auto run = [&](auto LAGc) {
+    bool pending = false;
+    for (int t = 0; t < t_main; t += NSTAGE)
+      static_for<NSTAGE>([&](auto STc) { tile(t + decltype(STc)::value, STc, LAGc, pending); });
+    if constexpr (decltype(LAGc)::value) {
+      if (pending) {  // tile t_main - 1 sits in stage NSTAGE - 1
+        bf16x8 pf[KB][2];
+        vphase(t_main - 1, s_cur, pf, std::false_type{});
+        m2(std::integral_constant<int, NSTAGE - 1>{}, pf);
       }
     }
+  };
+  if (lag) run(std::true_type{});
+  else run(std::false_type{});
+  int t = t_main;
 
-    // ---- online softmax; P^T fragments in bf16
-    bf16x8 pf[KB][2][QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][qb][i]);
-      mx = max_halves(mx) * c;
-      const bool raise = mx - m[qb] > TAU;  // false when mx == -inf
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-        const float alpha = raise ? fast_exp2(m[qb] - mx) : 1.f;
-        m[qb] = raise ? mx : m[qb];
-        lsum[qb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db) oacc[db][qb] *= alpha;
-      }
-      const float mc = m[qb] == -INFINITY ? 0.f : m[qb];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float p[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(fmaf(s[kb][qb][half * 8 + j], c, -mc));
-            lsum[qb] += p[j];
-          }
-          u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                     pack_bf16x2(p[6], p[7])};
-          pf[kb][half][qb] = as_bf16x8(w);
-        }
-    }
-
-    // ---- O^T += V^T * P^T; the transposing reads of d-block db+1 are in
-    // flight while the MFMAs of d-block db run.
-    {
-      const int g = (lane >> 4) & 1, s16 = lane & 15;
-      const int rsub = 4 * hi + (s16 >> 2);
-      const uint32_t vbase = lds_addr(vl);
-      auto vread = [&](int db, u32x2 (&r)[KB * 4]) {
-        const int d = db * 32 + 16 * g + 4 * (s16 & 3);
-        const int chunk = d >> 3, boff = (d & 7) * 2;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int half = 0; half < 2; ++half)
-#pragma unroll
-            for (int e = 0; e < 2; ++e) {
-              const int rr = kb * 32 + half * 16 + 8 * e + rsub;
-              r[(kb * 2 + half) * 2 + e] =
-                  lds_read_tr16_async<0>(vbase + (rr * CPR + swz<CPR>(rr, chunk)) * 16 + boff);
-            }
-      };
-      u32x2 vr[2][KB * 4];
-      vread(0, vr[0]);
-      wait_lds_tied(vr[0]);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        if (db + 1 < DB) vread(db + 1, vr[(db + 1) & 1]);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int x = (kb * 2 + half) * 2;
-            const bf16x8 vf = cat_tr(vr[db & 1][x], vr[db & 1][x + 1]);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) oacc[db][qb] = mfma32(vf, pf[kb][half][qb], oacc[db][qb]);
-          }
-        if (db + 1 < DB) wait_lds_tied(vr[(db + 1) & 1]);
-      }
-    }
+  // the remaining tiles run without the lag (both groups in step)
+  auto tile_step = [&](int tt, auto STc) {
+    constexpr int ST = decltype(STc)::value;
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    barrier();
+    if (tt + 1 < nt) issue(tt + 1, std::integral_constant<int, (ST + 1) % NSTAGE>{});
+    if (CAUSAL && tt * BC > wave_kv_last) return;
+    bf16x8 pf[KB][2];
+    m1(STc, s_cur);
+    vphase(tt, s_cur, pf, std::true_type{});
+    m2(STc, pf);
+  };
+  for (; t < nt; ++t) {
+    const int st = t % NSTAGE;
+    if (st == 0) tile_step(t, std::integral_constant<int, 0>{});
+    else if (st == 1) tile_step(t, std::integral_constant<int, 1>{});
+    else tile_step(t, std::integral_constant<int, 2>{});
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l = sum_halves(lsum[qb]);
-    const int row = wrow0 + qb * 32 + col;
+  {
+    const float l = sum_halves(lsum);
+    const int row = wrow0 + col;
     if (row < Sq) {
       const float inv = l > 0.f ? 1.f / l : 0.f;
       uint16_t* orow = a.o + ((size_t)bh * Sq + row) * D;
@@ -271,20 +330,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d = db * 32 + 8 * g4 + 4 * hi;
-          u32x2 w = {pack_bf16x2(oacc[db][qb][g4 * 4 + 0] * inv, oacc[db][qb][g4 * 4 + 1] * inv),
-                     pack_bf16x2(oacc[db][qb][g4 * 4 + 2] * inv, oacc[db][qb][g4 * 4 + 3] * inv)};
+          u32x2 w = {pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv),
+                     pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
           *(u32x2*)(orow + d) = w;
         }
-      if (hi == 0) a.lse[(size_t)bh * Sq + row] = l > 0.f ? (m[qb] + __log2f(l)) * kLn2 : -INFINITY;
+      if (hi == 0) a.lse[(size_t)bh * Sq + row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
   }
 }
 
-template <int D, int NW, int QB, int BC, bool CAUSAL>
+template <int D, int NW, int BC, bool CAUSAL>
 static hipError_t launch_one(const MhaArgs& a, hipStream_t stream) {
-  constexpr int BR = NW * QB * 32;
-  constexpr size_t lds = 2 * 2 * (size_t)BC * D * 2;
-  auto kern = mha_fwd_bf16_kernel<D, NW, QB, BC, CAUSAL>;
+  constexpr int BR = NW * 32;
+  constexpr int NSTAGE = 3;
+  constexpr size_t lds = 2 * (size_t)NSTAGE * BC * D * 2;
+  auto kern = mha_fwd_bf16_kernel<D, NW, BC, NSTAGE, CAUSAL>;
   // Thread-safe one-time opt-in to more than the default dynamic LDS.
   static const hipError_t attr_err =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -311,10 +371,18 @@ hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void
   a.Skv = Skv;
   a.n_bh = B * H;
   a.c = scale * kLog2e;
-  if (D == 128) {
-    return causal ? launch_one<128, 4, 1, 64, true>(a, stream) : launch_one<128, 4, 1, 64, false>(a, stream);
+  // Waves per workgroup (32 query rows each): 8 by default; TATTN_MHA_WAVES=4
+  // selects the 4-wave variant (for measurements).
+  static const int nw = [] {
+    const char* e = std::getenv("TATTN_MHA_WAVES");
+    return (e && std::atoi(e) == 4) ? 4 : 8;
+  }();
+  if (nw == 4) {
+    if (D == 128) return causal ? launch_one<128, 4, 64, true>(a, stream) : launch_one<128, 4, 64, false>(a, stream);
+    return causal ? launch_one<64, 4, 64, true>(a, stream) : launch_one<64, 4, 64, false>(a, stream);
   }
-  return causal ? launch_one<64, 4, 1, 64, true>(a, stream) : launch_one<64, 4, 1, 64, false>(a, stream);
+  if (D == 128) return causal ? launch_one<128, 8, 64, true>(a, stream) : launch_one<128, 8, 64, false>(a, stream);
+  return causal ? launch_one<64, 8, 64, true>(a, stream) : launch_one<64, 8, 64, false>(a, stream);
 }
 
 }  // namespace tattn
