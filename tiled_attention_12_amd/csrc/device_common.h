@@ -110,6 +110,14 @@ __device__ __forceinline__ u32x2 lds_read_tr16_async(uint32_t lds_addr) {
 __device__ __forceinline__ void wait_lds_tied(u32x2& a, u32x2& b) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
 }
+// s_waitcnt lgkmcnt(N) tied to two values: they are complete once at most N
+// later LDS operations are still outstanding (LDS operations complete in
+// order; the caller must have no scalar-memory loads in flight).
+template <int N>
+__device__ __forceinline__ void wait_lds_tied_n(u32x2& a, u32x2& b) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
+}
 __device__ __forceinline__ void wait_lds_tied(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 }

@@ -34,6 +34,15 @@
 #include "device_common.h"
 #include "launch.h"
 
+// Wave priority while issuing the MFMA phases (0 = leave the default).
+#ifndef TATTN_MFMA_PRIO
+#define TATTN_MFMA_PRIO 0
+#endif
+// 1: the second half of the waves runs one phase behind (see the tile loop)
+#ifndef TATTN_PINGPONG
+#define TATTN_PINGPONG 1
+#endif
+
 namespace tattn {
 
 struct MhaArgs {
@@ -164,6 +173,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   //   M1: S^T = K*Q^T (MFMA), V: masks + online softmax (VALU), M2: O^T += V^T*P^T (MFMA)
   auto m1 = [&](auto STc, f32x16 (&s)[KB]) {
     constexpr int ST = decltype(STc)::value;
+    if constexpr (TATTN_MFMA_PRIO > 0) __builtin_amdgcn_s_setprio(TATTN_MFMA_PRIO);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
     // k-steps in groups of 2; inside a group the key blocks alternate, so
@@ -184,6 +194,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   auto vphase = [&](int t, f32x16 (&s)[KB], bf16x8 (&pf)[KB][2], auto MASKEDc) {
+    if constexpr (TATTN_MFMA_PRIO > 0) __builtin_amdgcn_s_setprio(0);
     const int kv0 = t * BC;
     if constexpr (decltype(MASKEDc)::value) {
       const int lim = CAUSAL ? min(Skv - 1, wrow0 + col + Skv - Sq) : Skv - 1;
@@ -226,6 +237,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   auto m2 = [&](auto STc, const bf16x8 (&pf)[KB][2]) {
     constexpr int ST = decltype(STc)::value;
+    if constexpr (TATTN_MFMA_PRIO > 0) __builtin_amdgcn_s_setprio(TATTN_MFMA_PRIO);
     // for each 16-key slice: read the V^T fragments of all d-blocks, then one
     // MFMA per d-block (independent accumulators back to back)
     static_for<KB * 2>([&](auto SC) {
@@ -246,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // Each group's VALU phase then overlaps the other group's MFMA phases.
   // Tile t-1 stays readable until barrier t+1 because the ring has three
   // stages and the refill issued at barrier t targets stage (t+1) % 3.
-  const bool lag = wave >= NW / 2;
+  const bool lag = TATTN_PINGPONG && wave >= NW / 2;
   f32x16 s_cur[KB];   // scores of the tile in flight (group 1: of tile t-1 across the barrier)
 
   // One tile step of a group; LAG is a compile-time copy per group so the

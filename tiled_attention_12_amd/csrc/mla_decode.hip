@@ -15,10 +15,13 @@
 //              contiguous slice of the packed tile range (a slice may span
 //              batches) and, for each batch it touches, writes the
 //              normalised partial output O_s and its log-sum-exp lse_s into
-//              slot (workgroup + batch), which is unique per piece.
+//              slot (slice + batch), which is unique per piece.
 //  3. combine: for every (batch, head), lse = ln sum_s exp(lse_s) and
 //              O = sum_s exp(lse_s - lse) * O_s, rounded to bf16. This merge
 //              is exact: each O_s is normalised by its own exp(lse_s).
+//  Slices are numbered so that consecutive slices run on the same XCD (the
+//  hardware hands workgroup i to XCD i % 8): the pieces of one batch then
+//  share that XCD's L2 for Q.
 //
 // gfx950 mapping of the split kernel: 4 waves x 32 heads (H = 128); wave w
 // holds Q^T of its heads in registers (B operand, 36 k-steps of 16) and the
@@ -55,6 +58,11 @@ struct MlaArgs {
   float* part_o;    // [(P + B) * H * 512]
 };
 
+// Slice index of physical workgroup w: consecutive slices on one XCD.
+__device__ __forceinline__ int slice_of(int w, int P) {
+  return (P & 7) ? w : (w & 7) * (P >> 3) + (w >> 3);
+}
+
 __device__ __forceinline__ int batch_tiles(const int32_t* indptr, int b) {
   const int len = indptr[b + 1] - indptr[b];
   return len > 0 ? (len + kBK - 1) / kBK : 0;
@@ -73,13 +81,14 @@ __device__ __forceinline__ int split_owner(int g, int T, int P) {
   return w;
 }
 
-__global__ __launch_bounds__(1024) void mla_plan_kernel(const int32_t* indptr, int B, int* tile_ptr) {
+__global__ __launch_bounds__(1024) void mla_plan_kernel(MlaArgs a) {
   __shared__ int sums[1024];
+  const int B = a.B;
   const int t = threadIdx.x;
   const int per = (B + 1023) / 1024;
   const int b0 = min(B, t * per), b1 = min(B, b0 + per);
   int local = 0;
-  for (int b = b0; b < b1; ++b) local += batch_tiles(indptr, b);
+  for (int b = b0; b < b1; ++b) local += batch_tiles(a.indptr, b);
   sums[t] = local;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -90,10 +99,57 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(const int32_t* indptr, i
   }
   int run = t > 0 ? sums[t - 1] : 0;
   for (int b = b0; b < b1; ++b) {
-    tile_ptr[b] = run;
-    run += batch_tiles(indptr, b);
+    a.tile_ptr[b] = run;
+    run += batch_tiles(a.indptr, b);
   }
-  if (t == 1023) tile_ptr[B] = sums[1023];
+  if (t == 1023) a.tile_ptr[B] = sums[1023];
+}
+
+// Combine: one workgroup of 256 threads per (batch, 8 heads); thread t owns
+// head 8*blockIdx.y + t/32 and latent columns 16*(t%32) .. +15. Pieces of
+// empty slices between the two owners wrote nothing and are skipped.
+__global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a, int P) {
+  const int b = blockIdx.x;
+  const int H = a.H;
+  const int h = blockIdx.y * 8 + (threadIdx.x >> 5);
+  const int c0 = 16 * (threadIdx.x & 31);
+  const int T = a.tile_ptr[a.B];
+  const int g0 = a.tile_ptr[b], g1 = a.tile_ptr[b + 1];
+  if (h >= H) return;
+  if (g0 >= g1) {  // a batch without keys: O = 0, LSE = -inf
+    uint16_t* orow = a.o + ((size_t)b * H + h) * kDl + c0;
+    *(u32x4*)orow = u32x4{0u, 0u, 0u, 0u};
+    *(u32x4*)(orow + 8) = u32x4{0u, 0u, 0u, 0u};
+    if ((threadIdx.x & 31) == 0) a.lse[(size_t)b * H + h] = -INFINITY;
+    return;
+  }
+  const int w0 = split_owner(g0, T, P), w1 = split_owner(g1 - 1, T, P);
+  float mx = -INFINITY;
+  for (int v = w0; v <= w1; ++v) {
+    if (split_start(v, T, P) == split_start(v + 1, T, P)) continue;
+    mx = fmaxf(mx, a.part_lse[((size_t)v + b) * H + h]);
+  }
+  f32x4 acc[4] = {};
+  float tot = 0.f;
+  for (int v = w0; v <= w1; ++v) {
+    if (split_start(v, T, P) == split_start(v + 1, T, P)) continue;
+    const size_t slot = (size_t)v + b;
+    const float ls = a.part_lse[slot * H + h];
+    const float wt = ls == -INFINITY ? 0.f : __expf(ls - mx);
+    tot += wt;
+    const f32x4* src = (const f32x4*)(a.part_o + (slot * H + h) * kDl + c0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += wt * src[i];
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  uint16_t* orow = a.o + ((size_t)b * H + h) * kDl + c0;
+  u32x4 o0 = {pack_bf16x2(acc[0][0] * inv, acc[0][1] * inv), pack_bf16x2(acc[0][2] * inv, acc[0][3] * inv),
+              pack_bf16x2(acc[1][0] * inv, acc[1][1] * inv), pack_bf16x2(acc[1][2] * inv, acc[1][3] * inv)};
+  u32x4 o1 = {pack_bf16x2(acc[2][0] * inv, acc[2][1] * inv), pack_bf16x2(acc[2][2] * inv, acc[2][3] * inv),
+              pack_bf16x2(acc[3][0] * inv, acc[3][1] * inv), pack_bf16x2(acc[3][2] * inv, acc[3][3] * inv)};
+  *(u32x4*)orow = o0;
+  *(u32x4*)(orow + 8) = o1;
+  if ((threadIdx.x & 31) == 0) a.lse[(size_t)b * H + h] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
 }
 
 template <int NW, int NSTAGE>
@@ -139,7 +195,7 @@ void mla_split_kernel(MlaArgs a) {
     }
   }
 
-  const int w = blockIdx.x, P = gridDim.x;
+  const int P = gridDim.x, w = slice_of(blockIdx.x, P);
   const int T = a.tile_ptr[a.B];
   int g = split_start(w, T, P);
   const int gend = split_start(w + 1, T, P);
@@ -281,30 +337,33 @@ void mla_split_kernel(MlaArgs a) {
         }
       }
 
-      // ---- O^T += KV^T * P^T (KV^T by transposing reads of the latent tile);
-      // the reads of block db+1 are in flight while block db's MFMAs run.
+      // ---- O^T += KV^T * P^T (KV^T by transposing reads of the latent tile):
+      // half 0 of every d-block, then half 1, so consecutive MFMAs use
+      // different accumulators; the reads of the next step are in flight
+      // while the current MFMA runs.
       {
         uint32_t vb[2][4];
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
           for (int r = 0; r < 4; ++r) vb[e][r] = sbase + tbase[e][r];
-        auto vread = [&](auto DBc, u32x2 (&r)[4]) {
-          constexpr int db = decltype(DBc)::value;
-          r[0] = lds_read_tr16_async<(db >> 2) * 256>(vb[0][db & 3]);
-          r[1] = lds_read_tr16_async<(db >> 2) * 256>(vb[1][db & 3]);
-          r[2] = lds_read_tr16_async<16384 + (db >> 2) * 256>(vb[0][db & 3]);
-          r[3] = lds_read_tr16_async<16384 + (db >> 2) * 256>(vb[1][db & 3]);
+        constexpr int NSTEP = 2 * DB;
+        constexpr int AHEAD = 4;  // steps whose reads are in flight
+        auto vread = [&](auto SC, u32x2 (&r)[2]) {
+          constexpr int stp = decltype(SC)::value, half = stp / DB, db = stp % DB;
+          r[0] = lds_read_tr16_async<half * 16384 + (db >> 2) * 256>(vb[0][db & 3]);
+          r[1] = lds_read_tr16_async<half * 16384 + (db >> 2) * 256>(vb[1][db & 3]);
         };
-        u32x2 vr[2][4];
-        vread(std::integral_constant<int, 0>{}, vr[0]);
-        wait_lds_tied(vr[0]);
-        static_for<DB>([&](auto DBc) {
-          constexpr int db = decltype(DBc)::value;
-          if constexpr (db + 1 < DB) vread(std::integral_constant<int, db + 1>{}, vr[(db + 1) & 1]);
-          oacc[db] = mfma32(cat_tr(vr[db & 1][0], vr[db & 1][1]), pf[0], oacc[db]);
-          oacc[db] = mfma32(cat_tr(vr[db & 1][2], vr[db & 1][3]), pf[1], oacc[db]);
-          if constexpr (db + 1 < DB) wait_lds_tied(vr[(db + 1) & 1]);
+        u32x2 vr[AHEAD][2];
+        static_for<AHEAD>([&](auto SC) { vread(SC, vr[decltype(SC)::value]); });
+        static_for<NSTEP>([&](auto SC) {
+          constexpr int stp = decltype(SC)::value, half = stp / DB, db = stp % DB;
+          constexpr int slot = stp % AHEAD;
+          // reads of the later in-flight steps may still be outstanding
+          constexpr int later = (NSTEP - 1 - stp) < (AHEAD - 1) ? (NSTEP - 1 - stp) : (AHEAD - 1);
+          wait_lds_tied_n<2 * later>(vr[slot][0], vr[slot][1]);
+          oacc[db] = mfma32(cat_tr(vr[slot][0], vr[slot][1]), pf[half], oacc[db]);
+          if constexpr (stp + AHEAD < NSTEP) vread(std::integral_constant<int, stp + AHEAD>{}, vr[slot]);
         });
       }
     }
@@ -331,43 +390,6 @@ void mla_split_kernel(MlaArgs a) {
     if (g >= gend) break;
     do { ++b; } while (a.tile_ptr[b + 1] <= g);
   }
-}
-
-// One workgroup of 128 threads per (batch, head); thread t owns latent
-// columns 4t .. 4t+3.
-__global__ __launch_bounds__(128) void mla_combine_kernel(MlaArgs a, int P) {
-  const int bh = blockIdx.x;
-  const int b = bh / a.H, h = bh - b * a.H;
-  const int t = threadIdx.x;
-  const int T = a.tile_ptr[a.B];
-  const int g0 = a.tile_ptr[b], g1 = a.tile_ptr[b + 1];
-  uint16_t* orow = a.o + (size_t)bh * kDl + 4 * t;
-  if (g0 >= g1) {
-    *(u32x2*)orow = u32x2{0u, 0u};
-    if (t == 0) a.lse[bh] = -INFINITY;
-    return;
-  }
-  const int w0 = split_owner(g0, T, P), w1 = split_owner(g1 - 1, T, P);
-  // Workgroups between the two owners with an empty slice (possible when
-  // there are fewer tiles than workgroups) wrote nothing and are skipped.
-  float mx = -INFINITY;
-  for (int w = w0; w <= w1; ++w) {
-    if (split_start(w, T, P) == split_start(w + 1, T, P)) continue;
-    mx = fmaxf(mx, a.part_lse[((size_t)w + b) * a.H + h]);
-  }
-  float tot = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int w = w0; w <= w1; ++w) {
-    if (split_start(w, T, P) == split_start(w + 1, T, P)) continue;
-    const size_t slot = (size_t)w + b;
-    const float ls = a.part_lse[slot * a.H + h];
-    const float wt = ls == -INFINITY ? 0.f : __expf(ls - mx);
-    tot += wt;
-    acc += wt * *(const f32x4*)(a.part_o + (slot * a.H + h) * kDl + 4 * t);
-  }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  *(u32x2*)orow = u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  if (t == 0) a.lse[bh] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -404,11 +426,12 @@ hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, co
   a.c = scale * kLog2e;
   char* ws = (char*)workspace;
   const size_t slots = (size_t)n_split + B;
+  const size_t ints = align256((size_t)(B + 1) * 4);
   a.tile_ptr = (int*)ws;
-  a.part_lse = (float*)(ws + align256((size_t)(B + 1) * 4));
-  a.part_o = (float*)(ws + align256((size_t)(B + 1) * 4) + align256(slots * H * 4));
+  a.part_lse = (float*)(ws + ints);
+  a.part_o = (float*)(ws + ints + align256(slots * H * 4));
 
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, kv_indptr, B, a.tile_ptr);
+  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   switch (H) {
@@ -417,7 +440,7 @@ hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, co
     default: e = launch_split<1, 3>(a, n_split, stream); break;
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(B * H), dim3(128), 0, stream, a, n_split);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3(B, (H + 7) / 8), dim3(256), 0, stream, a, n_split);
   return hipGetLastError();
 }
 
