@@ -62,7 +62,8 @@ extern "C" {
  *   lse device, fp32 [B, H, Sq],      4-byte aligned, written
  *   B, H, Sq >= 0 (any of them 0: nothing to do, TATTN_OK); Skv >= 0
  *   D   head dimension: 64 or 128 (else TATTN_ERR_UNSUPPORTED)
- *   causal 0 or 1; scale any finite float (typically 1/sqrt(D))
+ *   causal 0 or 1; scale finite and > 0 (typically 1/sqrt(D)), else
+ *   TATTN_ERR_INVALID_ARG
  *
  * A row that sees no key (Skv == 0, or causal rows with i + Skv - Sq < 0)
  * gets O = 0 and LSE = -inf. q/k/v may overlap each other; o and lse must
@@ -102,18 +103,18 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
  *   k_pe      device, bf16 [N, 64],     16-byte aligned
  *   o         device, bf16 [B, H, 512], 16-byte aligned, written
  *   lse       device, fp32 [B, H],      4-byte aligned, written
- *   B >= 0 (0: nothing to do); H a multiple of 32 with 32 <= H <= 128
+ *   B >= 0 (0: nothing to do); H is 32, 64 or 128 (else TATTN_ERR_UNSUPPORTED)
  *   kv_indptr device, int32 [B+1], 4-byte aligned, read on the device only:
  *             kv_indptr[0] >= 0 and non-decreasing; the caller guarantees
  *             that rows up to kv_indptr[B] exist. A decreasing pair is
  *             treated as an empty batch.
- *   scale     any finite float (typically 1/sqrt(576))
+ *   scale     finite and > 0 (typically 1/sqrt(576)), else TATTN_ERR_INVALID_ARG
  *
  * A batch with no keys gets O = 0 and LSE = -inf. Work is split along the
  * packed key axis over the GPU's compute units; each piece writes a
  * normalised partial output and its log-sum-exp into a device workspace
  * that is allocated and freed in stream order on `stream`
- * ((CUs + B) * H * 513 * 4 bytes plus the split plan), and a second kernel
+ * ((CUs + B) * H * (512 * 2 + 4) bytes plus the split plan), and a second kernel
  * merges the pieces of each batch. TATTN_ERR_OOM if that workspace cannot
  * be allocated.
  */

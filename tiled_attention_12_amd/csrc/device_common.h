@@ -137,6 +137,20 @@ __device__ __forceinline__ void wait_lds_tied(u32x2 (&r)[N]) {
   }
 }
 
+// ds_read_b128 through inline asm (not counted by the compiler; wait with
+// wait_lds_tied_n4 before use).
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read128_async(uint32_t lds_addr) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFF));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void wait_lds_tied_n4(u32x4& a) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "i"(N));
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)(p);
 }

@@ -14,8 +14,8 @@
 //  2. split:   one persistent workgroup per compute unit takes an equal,
 //              contiguous slice of the packed tile range (a slice may span
 //              batches) and, for each batch it touches, writes the
-//              normalised partial output O_s and its log-sum-exp lse_s into
-//              slot (slice + batch), which is unique per piece.
+//              normalised partial output O_s (bf16) and its log-sum-exp lse_s
+//              (fp32) into slot (slice + batch), which is unique per piece.
 //  3. combine: for every (batch, head), lse = ln sum_s exp(lse_s) and
 //              O = sum_s exp(lse_s - lse) * O_s, rounded to bf16. This merge
 //              is exact: each O_s is normalised by its own exp(lse_s).
@@ -54,8 +54,8 @@ struct MlaArgs {
   int B, H;
   float c;          // scale * log2(e)
   int* tile_ptr;    // [B + 1]
-  float* part_lse;  // [(P + B) * H]
-  float* part_o;    // [(P + B) * H * 512]
+  float* part_lse;     // [(P + B) * H]
+  uint16_t* part_o;    // [(P + B) * H * 512] bf16
 };
 
 // Slice index of physical workgroup w: consecutive slices on one XCD.
@@ -137,9 +137,16 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a, int P) {
     const float ls = a.part_lse[slot * H + h];
     const float wt = ls == -INFINITY ? 0.f : __expf(ls - mx);
     tot += wt;
-    const f32x4* src = (const f32x4*)(a.part_o + (slot * H + h) * kDl + c0);
+    const u32x4* src = (const u32x4*)(a.part_o + (slot * H + h) * kDl + c0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += wt * src[i];
+    for (int i = 0; i < 2; ++i) {
+      const u32x4 x = src[i];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * i + k / 2][2 * (k % 2)] += wt * __uint_as_float(x[k] << 16);
+        acc[2 * i + k / 2][2 * (k % 2) + 1] += wt * __uint_as_float(x[k] & 0xffff0000u);
+      }
+    }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
   uint16_t* orow = a.o + ((size_t)b * H + h) * kDl + c0;
@@ -287,18 +294,21 @@ void mla_split_kernel(MlaArgs a) {
       const uint32_t sbase = lds_addr(sl);
       f32x16 s = f32x16{};
       {
-        constexpr int G = 4;
-        static_for<KS / G>([&](auto K0) {
-          constexpr int k0 = decltype(K0)::value * G;
-          bf16x8 kf[G];
-          static_for<G>([&](auto U) {
-            constexpr int ks = k0 + decltype(U)::value;
-            const uint32_t addr = ks < KSL ? sbase + kbase[ks & 7] + 256 * (ks >> 3) : sbase + pbase[ks - KSL];
-            kf[U] = as_bf16x8(lds_read128((const void*)(uintptr_t)addr));
-          });
-          static_for<G>([&](auto U) { s = mfma32(kf[U], qf[k0 + decltype(U)::value], s); });
-          __builtin_amdgcn_sched_group_barrier(0x100, G, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, G, 0);
+        // operand reads run AHEAD k-steps in front of their MFMAs
+        constexpr int AHEAD = 6;
+        auto kread = [&](auto KSc) -> u32x4 {
+          constexpr int ks = decltype(KSc)::value;
+          if constexpr (ks < KSL) return lds_read128_async<256 * (ks >> 3)>(sbase + kbase[ks & 7]);
+          else return lds_read128_async<0>(sbase + pbase[ks - KSL]);
+        };
+        u32x4 kr[AHEAD];
+        static_for<AHEAD>([&](auto KSc) { kr[decltype(KSc)::value] = kread(KSc); });
+        static_for<KS>([&](auto KSc) {
+          constexpr int ks = decltype(KSc)::value, slot = ks % AHEAD;
+          constexpr int later = (KS - 1 - ks) < (AHEAD - 1) ? (KS - 1 - ks) : (AHEAD - 1);
+          wait_lds_tied_n4<later>(kr[slot]);
+          s = mfma32(as_bf16x8(kr[slot]), qf[ks], s);
+          if constexpr (ks + AHEAD < KS) kr[slot] = kread(std::integral_constant<int, ks + AHEAD>{});
         });
       }
 
@@ -373,15 +383,14 @@ void mla_split_kernel(MlaArgs a) {
       const float l = sum_halves(lsum);
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const size_t slot = (size_t)w + b;
-      float* po = a.part_o + (slot * H + head) * kDl;
+      uint16_t* po = a.part_o + (slot * H + head) * kDl;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d = db * 32 + 8 * g4 + 4 * hi;
-          f32x4 v = {oacc[db][g4 * 4] * inv, oacc[db][g4 * 4 + 1] * inv, oacc[db][g4 * 4 + 2] * inv,
-                     oacc[db][g4 * 4 + 3] * inv};
-          *(f32x4*)(po + d) = v;
+          *(u32x2*)(po + d) = u32x2{pack_bf16x2(oacc[db][g4 * 4] * inv, oacc[db][g4 * 4 + 1] * inv),
+                                    pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
         }
       if (hi == 0) a.part_lse[slot * H + head] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
@@ -396,7 +405,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t mla_workspace_bytes(int B, int H, int n_split) {
   const size_t slots = (size_t)n_split + B;
-  return align256((size_t)(B + 1) * 4) + align256(slots * H * 4) + slots * H * kDl * 4;
+  return align256((size_t)(B + 1) * 4) + align256(slots * H * 4) + slots * H * kDl * 2;
 }
 
 template <int NW, int NSTAGE>
@@ -429,7 +438,7 @@ hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, co
   const size_t ints = align256((size_t)(B + 1) * 4);
   a.tile_ptr = (int*)ws;
   a.part_lse = (float*)(ws + ints);
-  a.part_o = (float*)(ws + ints + align256(slots * H * 4));
+  a.part_o = (uint16_t*)(ws + ints + align256(slots * H * 4));
 
   hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
