@@ -26,6 +26,29 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 N_COPIES = 3
 
+# HBM traffic per launch of the non-causal prefill kernel, from two
+# rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
+# each scaled by what the same counter reads for a plain 256 MiB device copy
+# in the same run (FETCH_SIZE read 131094 KiB for it: factor 2.0; WRITE_SIZE
+# read 262144 KiB: factor 1.0). The figures hold for the kernel sources they
+# were taken on; once those files change the field is reported as null.
+TRAFFIC_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip",
+                   "tiled_attention_12_amd/csrc/device_common.h")
+TRAFFIC = {"sources_sha256": "18b991e2c35ff8890bc5384d7711c394fd562c95b79626070043f4ad38bbf391",
+           "fetch_kib": 82110.0, "fetch_factor": 2.0, "write_kib": 33280.0, "write_factor": 1.0}
+
+
+def _traffic_bytes():
+    """Counter-measured HBM bytes per launch, or None if the kernel changed since."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != TRAFFIC["sources_sha256"]:
+        return None
+    return 1024.0 * (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_factor"] + TRAFFIC["write_kib"] * TRAFFIC["write_factor"])
+
 
 def _log(msg):
     print(msg, file=sys.stderr, flush=True)
@@ -51,19 +74,53 @@ def _copies(arrs, dev):
     return out
 
 
+class _Runahead:
+    """Keeps the GPU ahead of the host during a timed region.
+
+    A spin kernel (outside the timed region) holds the stream while the host
+    enqueues every timed launch, so the launches then run back to back and
+    the events around each one measure the GPU, not Python's launch rate.
+    After the region, check() warns if enqueueing outlasted the spin."""
+
+    SPIN_CYCLES = 200_000_000
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        torch.cuda.synchronize()
+        self.e0 = torch.cuda.Event(enable_timing=True)
+        self.e1 = torch.cuda.Event(enable_timing=True)
+        self.e0.record()
+        torch.cuda._sleep(self.SPIN_CYCLES)
+        self.e1.record()
+        self.t0 = time.perf_counter()
+
+    def enqueued(self):
+        self.t_enqueue = time.perf_counter() - self.t0
+
+    def check(self, what):
+        spin_ms = self.e0.elapsed_time(self.e1)
+        if self.t_enqueue * 1e3 > spin_ms:
+            _log(f"bench: warning: enqueueing {what} took {self.t_enqueue * 1e3:.1f} ms, longer than the "
+                 f"{spin_ms:.1f} ms spin; the GPU may have waited for the host")
+        return spin_ms
+
+
 def _time_launches(fn, sets, warmup, reps):
     """Average duration (ms) of fn(set) over reps launches, with HIP events on
     the stream the kernels are launched on (torch's current stream)."""
     import torch
     for i in range(warmup):
         fn(sets[i % len(sets)])
-    torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ra = _Runahead()
     ev[0].record()
     for i in range(reps):
         fn(sets[i % len(sets)])
         ev[i + 1].record()
+    ra.enqueued()
     torch.cuda.synchronize()
+    ra.check("the launches")
     d = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
     return float(np.mean(d)), float(np.median(d)), float(np.min(d))
 
@@ -194,8 +251,7 @@ def main():
     torch.cuda.synchronize()
     # per-launch events: non-causal launch j is bracketed by ev[2j], ev[2j+1]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
+    ra = _Runahead()
     ev[0].record()
     for i in range(args.steps):
         s = sets[i % N_COPIES]
@@ -203,8 +259,10 @@ def main():
         ev[2 * i + 1].record()
         ta.attn_fwd(s["q"], s["k"], s["v"], causal=True, scale=w["scale"], out=o_buf, lse=l_buf)
         ev[2 * i + 2].record()
+    ra.enqueued()
     torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
+    spin_ms = ra.check("the timed steps")
+    t_wall = ra.t_enqueue
     d_nc = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)]
     d_c = [ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)]
     total_ms = ev[0].elapsed_time(ev[-1])
@@ -212,7 +270,7 @@ def main():
     value = (f_nc + f_c) / (ms_step * 1e-3) / 1e12
     nc_ms, c_ms = float(np.mean(d_nc)), float(np.mean(d_c))
     _log(f"bench: prefill non-causal {nc_ms * 1e3:.1f} us, causal {c_ms * 1e3:.1f} us, "
-         f"step {ms_step * 1e3:.1f} us, wall {t_wall:.3f} s")
+         f"step {ms_step * 1e3:.1f} us, host enqueue {t_wall * 1e3:.1f} ms under a {spin_ms:.1f} ms spin")
 
     workloads = {
         "mha_prefill_bf16_noncausal": {
@@ -272,8 +330,8 @@ def main():
         "config": {"workload": "mha_prefill_bf16: B=4 H=16 Sq=Skv=2048 D=128, non-causal + causal per step",
                    "global_batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "mha_fwd_bf16_kernel<128,4,1,64,false> (non-causal)",
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": _traffic_bytes(),
+                     "kernel": "mha_fwd_bf16_kernel<128, 8, 64, 3, false> (non-causal)",
                      "alg_flops_per_launch": f_nc, "alg_bytes_per_launch": nbytes},
         "workloads": workloads,
     }

@@ -1,0 +1,65 @@
+"""Host-side logic of the benchmark: work accounting, the traffic guard and
+the one-GPU rule. No GPU needed."""
+
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+from tiled_attention_12_amd.workloads import mha_bytes, mha_flops, mla_bytes, mla_flops  # noqa: E402
+
+
+@pytest.mark.parametrize("Sq,Skv", [(1, 1), (5, 5), (7, 3), (3, 7), (64, 200)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_mha_flops_counts_visible_pairs(Sq, Skv, causal):
+    # brute force over (i, j): row i sees key j unless causal and j > i + Skv - Sq
+    pairs = sum(1 for i in range(Sq) for j in range(Skv) if not causal or j <= i + Skv - Sq)
+    D = 16
+    assert mha_flops(2, 3, Sq, Skv, D, causal) == 2 * 2 * 3 * pairs * (D + D)
+
+
+def test_mha_flops_headline_values():
+    # non-causal: 4 * B * H * S^2 * D; causal: S(S+1)/2 pairs per head
+    assert mha_flops(4, 16, 2048, 2048, 128, False) == 4 * 4 * 16 * 2048 * 2048 * 128
+    assert mha_flops(4, 16, 2048, 2048, 128, True) == 4 * 4 * 16 * (2048 * 2049 // 2) * 128
+
+
+def test_byte_counts():
+    # Q, K, V, O in bf16 plus an fp32 LSE per row
+    assert mha_bytes(4, 16, 2048, 2048, 128, 2) == 4 * (4 * 16 * 2048 * 128 * 2) + 4 * 16 * 2048 * 4
+    # MLA: 576-wide bf16 key rows, 576-wide queries, 512-wide bf16 outputs, fp32 LSE
+    assert mla_bytes(64, 128, 262144) == 1152 * 262144 + 1152 * 64 * 128 + 1024 * 64 * 128 + 4 * 64 * 128
+    assert mla_flops(128, 10) == 2 * 128 * 1088 * 10
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_traffic_is_null_once_the_kernel_sources_change(monkeypatch):
+    import bench
+    t = bench._traffic_bytes()
+    if t is not None:
+        tr = bench.TRAFFIC
+        assert t == pytest.approx(1024 * (tr["fetch_kib"] * tr["fetch_factor"] + tr["write_kib"] * tr["write_factor"]))
+        # the written bytes can never be fewer than O (bf16) and LSE (fp32) of the headline launch
+        assert tr["write_kib"] * tr["write_factor"] * 1024 >= 4 * 16 * 2048 * (128 * 2 + 4)
+    monkeypatch.setitem(bench.TRAFFIC, "sources_sha256", "0" * 64)
+    assert bench._traffic_bytes() is None
+
+
+def test_cpu_baseline_budget_is_bounded(monkeypatch):
+    import bench
+    out = bench._cpu_baseline(budget_s=0.5)
+    assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s"
+    assert out["value"] > 0 and out["cores"] >= 1
+    assert np.isfinite(out["value"])
