@@ -6,9 +6,10 @@
 // accumulator, O = acc / l), with the exponentials taken in base 2 after
 // folding scale*log2(e) into one multiply, as "TileLang programming model and
 // FlashMLA" (section 3.1) does. The K/V tile loop is software pipelined over
-// two LDS stages (section 2.2 there).
+// LDS stages (section 2.2 there).
 //
-// gfx950 mapping (one workgroup = NW waves = NW*QB*32 query rows):
+// gfx950 mapping (one workgroup = NW waves = NW*32 query rows, two waves per
+// SIMD):
 //  * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16. Q^T is the B operand and is
 //    loaded once into registers; K comes from LDS as the A operand. With S
 //    transposed, lane l owns query column l%32 and 16 of the 32 keys of each
@@ -19,9 +20,15 @@
 //    A operand's); V^T is read from the row-major V tile by
 //    ds_read_b64_tr_b16. O^T keeps lane l on query l%32, so the rescale and
 //    the final 1/l are per-lane multiplies.
-//  * K/V tiles move HBM -> LDS with global_load_lds_dwordx4 (no VGPR round
-//    trip) into an XOR-swizzled layout, double buffered; one barrier per
-//    tile.
+//  * K/V tiles of 64 keys move HBM -> LDS with global_load_lds_dwordx4 (no
+//    VGPR round trip) into an XOR-swizzled layout, through a ring of three
+//    stages; one barrier per tile. Every LDS address is a per-lane base plus
+//    an instruction offset (stage, key block, row half).
+//  * The two waves of a SIMD run offset by a phase: waves 0..NW/2-1 run
+//    scores(t), softmax(t), P*V(t) after barrier t; waves NW/2.. run
+//    softmax(t-1), P*V(t-1), scores(t), so one wave's VALU phase overlaps the
+//    other's MFMA phases. Tiles that need masks (causal diagonal, ragged
+//    tail) run in step afterwards.
 //  * The running max is only raised when a new score exceeds it by more than
 //    2^8 (in base-2 units), so the O rescale runs on few tiles; every
 //    exponential stays <= 2^8 and the result is unchanged (both O and l are
@@ -29,19 +36,8 @@
 //  * Workgroup -> tile order: the hardware hands workgroup i to XCD i % 8;
 //    all query tiles of a (batch, head) are sent to one XCD so its K/V stays
 //    in that XCD's L2, and causal launches run the longest tiles first.
-#include <cstdlib>
-
 #include "device_common.h"
 #include "launch.h"
-
-// Wave priority while issuing the MFMA phases (0 = leave the default).
-#ifndef TATTN_MFMA_PRIO
-#define TATTN_MFMA_PRIO 0
-#endif
-// 1: the second half of the waves runs one phase behind (see the tile loop)
-#ifndef TATTN_PINGPONG
-#define TATTN_PINGPONG 1
-#endif
 
 namespace tattn {
 
@@ -173,7 +169,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   //   M1: S^T = K*Q^T (MFMA), V: masks + online softmax (VALU), M2: O^T += V^T*P^T (MFMA)
   auto m1 = [&](auto STc, f32x16 (&s)[KB]) {
     constexpr int ST = decltype(STc)::value;
-    if constexpr (TATTN_MFMA_PRIO > 0) __builtin_amdgcn_s_setprio(TATTN_MFMA_PRIO);
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
     // k-steps in groups of 2; inside a group the key blocks alternate, so
@@ -194,7 +189,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   auto vphase = [&](int t, f32x16 (&s)[KB], bf16x8 (&pf)[KB][2], auto MASKEDc) {
-    if constexpr (TATTN_MFMA_PRIO > 0) __builtin_amdgcn_s_setprio(0);
     const int kv0 = t * BC;
     if constexpr (decltype(MASKEDc)::value) {
       const int lim = CAUSAL ? min(Skv - 1, wrow0 + col + Skv - Sq) : Skv - 1;
@@ -237,7 +231,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   auto m2 = [&](auto STc, const bf16x8 (&pf)[KB][2]) {
     constexpr int ST = decltype(STc)::value;
-    if constexpr (TATTN_MFMA_PRIO > 0) __builtin_amdgcn_s_setprio(TATTN_MFMA_PRIO);
     // for each 16-key slice: read the V^T fragments of all d-blocks, then one
     // MFMA per d-block (independent accumulators back to back)
     static_for<KB * 2>([&](auto SC) {
@@ -258,7 +251,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // Each group's VALU phase then overlaps the other group's MFMA phases.
   // Tile t-1 stays readable until barrier t+1 because the ring has three
   // stages and the refill issued at barrier t targets stage (t+1) % 3.
-  const bool lag = TATTN_PINGPONG && wave >= NW / 2;
+  const bool lag = wave >= NW / 2;
   f32x16 s_cur[KB];   // scores of the tile in flight (group 1: of tile t-1 across the barrier)
 
   // One tile step of a group; LAG is a compile-time copy per group so the
@@ -383,16 +376,6 @@ hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void
   a.Skv = Skv;
   a.n_bh = B * H;
   a.c = scale * kLog2e;
-  // Waves per workgroup (32 query rows each): 8 by default; TATTN_MHA_WAVES=4
-  // selects the 4-wave variant (for measurements).
-  static const int nw = [] {
-    const char* e = std::getenv("TATTN_MHA_WAVES");
-    return (e && std::atoi(e) == 4) ? 4 : 8;
-  }();
-  if (nw == 4) {
-    if (D == 128) return causal ? launch_one<128, 4, 64, true>(a, stream) : launch_one<128, 4, 64, false>(a, stream);
-    return causal ? launch_one<64, 4, 64, true>(a, stream) : launch_one<64, 4, 64, false>(a, stream);
-  }
   if (D == 128) return causal ? launch_one<128, 8, 64, true>(a, stream) : launch_one<128, 8, 64, false>(a, stream);
   return causal ? launch_one<64, 8, 64, true>(a, stream) : launch_one<64, 8, 64, false>(a, stream);
 }
