@@ -29,13 +29,13 @@ N_COPIES = 3
 # HBM traffic per launch of the non-causal prefill kernel, from two
 # rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
 # each scaled by what the same counter reads for a plain 256 MiB device copy
-# in the same run (FETCH_SIZE read 131094 KiB for it: factor 2.0; WRITE_SIZE
+# in the same run (FETCH_SIZE read 131093 KiB for it: factor 2.0; WRITE_SIZE
 # read 262144 KiB: factor 1.0). The figures hold for the kernel sources they
 # were taken on; once those files change the field is reported as null.
 TRAFFIC_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip",
                    "tiled_attention_12_amd/csrc/device_common.h")
-TRAFFIC = {"sources_sha256": "18b991e2c35ff8890bc5384d7711c394fd562c95b79626070043f4ad38bbf391",
-           "fetch_kib": 82110.0, "fetch_factor": 2.0, "write_kib": 33280.0, "write_factor": 1.0}
+TRAFFIC = {"sources_sha256": "a93373d9869721eb1f86d7e29472125702cbfce91fcd41558ac8f7e609c2aa14",
+           "fetch_kib": 82104.0, "fetch_factor": 2.0, "write_kib": 33282.0, "write_factor": 1.0}
 
 
 def _traffic_bytes():

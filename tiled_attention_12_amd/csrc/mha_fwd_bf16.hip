@@ -24,11 +24,11 @@
 //    VGPR round trip) into an XOR-swizzled layout, through a ring of three
 //    stages; one barrier per tile. Every LDS address is a per-lane base plus
 //    an instruction offset (stage, key block, row half).
-//  * The two waves of a SIMD run offset by a phase: waves 0..NW/2-1 run
-//    scores(t), softmax(t), P*V(t) after barrier t; waves NW/2.. run
-//    softmax(t-1), P*V(t-1), scores(t), so one wave's VALU phase overlaps the
-//    other's MFMA phases. Tiles that need masks (causal diagonal, ragged
-//    tail) run in step afterwards.
+//  * Each wave runs one tile behind itself: after barrier t it forms the
+//    scores of tile t on the MFMAs while the VALU exponentiates the scores of
+//    tile t-1 (instruction groups interleaved with sched_group_barrier), then
+//    accumulates P*V of tile t-1. Tiles that need masks (causal diagonal,
+//    ragged tail) run unpipelined afterwards.
 //  * The running max is only raised when a new score exceeds it by more than
 //    2^8 (in base-2 units), so the O rescale runs on few tiles; every
 //    exponential stays <= 2^8 and the result is unchanged (both O and l are
@@ -38,6 +38,16 @@
 //    in that XCD's L2, and causal launches run the longest tiles first.
 #include "device_common.h"
 #include "launch.h"
+
+// K/V ring depth: 3 (prefetch one tile ahead) or 4 (two tiles ahead)
+#ifndef TATTN_MHA_STAGES
+#define TATTN_MHA_STAGES 3
+#endif
+// VALU instructions scheduled between consecutive score MFMAs
+#ifndef TATTN_VALU_PER_MFMA
+#define TATTN_VALU_PER_MFMA 4
+#endif
+
 
 namespace tattn {
 
@@ -68,7 +78,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int LPT = 2 * LOADS;   // loads per wave per tile (K and V)
   static_assert(BC * CPR % (64 * NW) == 0, "tile must split into whole wave loads");
   static_assert(NSTAGE * TILE <= 65536, "LDS offsets must fit the 16-bit instruction offset");
-  static_assert(NSTAGE == 3, "three LDS stages: the lagging wave group reads tile t-1 after barrier t");
+  // Tile t+PF is loaded while tile t is scored and tile t-1 accumulated, so
+  // the ring needs PF + 2 stages.
+  constexpr int PF = NSTAGE - 2;
+  static_assert(PF == 1 || PF == 2, "prefetch distance 1 or 2");
+  constexpr int UN = NSTAGE % 2 == 0 ? NSTAGE : 2 * NSTAGE;  // unroll: stages x score sets
   constexpr float TAU = 8.0f;
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -146,7 +160,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
-  if (nt > 0) issue(0, std::integral_constant<int, 0>{});
+  static_for<PF>([&](auto Ic) {
+    if (decltype(Ic)::value < nt) issue(decltype(Ic)::value, Ic);
+  });
+  // wait until this wave's loads of tile t have landed (tiles up to
+  // t + PF - 1 may still be in flight)
+  auto wait_tile = [&](int t) {
+    if constexpr (PF == 2) {
+      if (t + 1 < nt) {
+        wait_vmcnt<LPT>();
+        return;
+      }
+    }
+    wait_vmcnt<0>();
+  };
 
   // Q^T fragments (B operand), loaded once.
   bf16x8 qf[KS];
@@ -172,23 +199,30 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
     // k-steps in groups of 2; inside a group the key blocks alternate, so
-    // consecutive MFMAs never depend on each other
-    static_for<KS / 2>([&](auto Gc) {
+    // consecutive MFMAs never depend on each other. The K fragments of group
+    // g+1 are read while group g's MFMAs run.
+    auto rd = [&](auto Gc, bf16x8 (&kf)[2][KB]) {
       constexpr int g = decltype(Gc)::value;
-      bf16x8 kf[2][KB];
       static_for<2>([&](auto Uc) {
         static_for<KB>([&](auto KBc) {
           kf[Uc][KBc] = as_bf16x8(lds_read128(
               (const void*)(uintptr_t)(kbase[2 * g + Uc] + ST * TILE + decltype(KBc)::value * 32 * RS)));
         });
       });
+    };
+    bf16x8 kf[2][2][KB];
+    rd(std::integral_constant<int, 0>{}, kf[0]);
+    static_for<KS / 2>([&](auto Gc) {
+      constexpr int g = decltype(Gc)::value;
+      if constexpr (g + 1 < KS / 2) rd(std::integral_constant<int, g + 1>{}, kf[(g + 1) % 2]);
       static_for<2>([&](auto Uc) {
-        static_for<KB>([&](auto KBc) { s[KBc] = mfma32(kf[Uc][KBc], qf[2 * g + Uc], s[KBc]); });
+        static_for<KB>([&](auto KBc) { s[KBc] = mfma32(kf[g % 2][Uc][KBc], qf[2 * g + Uc], s[KBc]); });
       });
     });
   };
 
-  auto vphase = [&](int t, f32x16 (&s)[KB], bf16x8 (&pf)[KB][2], auto MASKEDc) {
+  // V, first part: masks, tile max, and (rarely) raising the running max
+  auto vmax = [&](int t, f32x16 (&s)[KB], auto MASKEDc) {
     const int kv0 = t * BC;
     if constexpr (decltype(MASKEDc)::value) {
       const int lim = CAUSAL ? min(Skv - 1, wrow0 + col + Skv - Sq) : Skv - 1;
@@ -212,6 +246,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
     }
+  };
+  // V, second part: exponentials, row sums, P^T in bf16
+  auto vexp = [&](const f32x16 (&s)[KB], bf16x8 (&pf)[KB][2]) {
     const float mc = m == -INFINITY ? 0.f : m;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
@@ -227,6 +264,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                    pack_bf16x2(p[6], p[7])};
         pf[kb][half] = as_bf16x8(w);
       }
+  };
+  auto vphase = [&](int t, f32x16 (&s)[KB], bf16x8 (&pf)[KB][2], auto MASKEDc) {
+    vmax(t, s, MASKEDc);
+    vexp(s, pf);
   };
 
   auto m2 = [&](auto STc, const bf16x8 (&pf)[KB][2]) {
@@ -246,81 +287,83 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     });
   };
 
-  // Two wave groups share each SIMD: group 0 (waves 0..NW/2-1) runs
-  // M1(t) V(t) M2(t) after barrier t; group 1 runs V(t-1) M2(t-1) M1(t).
-  // Each group's VALU phase then overlaps the other group's MFMA phases.
-  // Tile t-1 stays readable until barrier t+1 because the ring has three
-  // stages and the refill issued at barrier t targets stage (t+1) % 3.
-  const bool lag = wave >= NW / 2;
-  f32x16 s_cur[KB];   // scores of the tile in flight (group 1: of tile t-1 across the barrier)
-
-  // One tile step of a group; LAG is a compile-time copy per group so the
-  // two groups' loops are allocated independently.
-  auto tile = [&](int t, auto STc, auto LAGc, bool& pending) {
-    constexpr int ST = decltype(STc)::value;
-    constexpr int SP = (ST + NSTAGE - 1) % NSTAGE;  // stage of tile t-1
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    barrier();
-    if (t + 1 < nt) issue(t + 1, std::integral_constant<int, (ST + 1) % NSTAGE>{});
-    if constexpr (!decltype(LAGc)::value) {
-      bf16x8 pf[KB][2];
-      m1(STc, s_cur);
-      vphase(t, s_cur, pf, std::false_type{});
-      m2(STc, pf);
-    } else {
-      if (pending) {
-        bf16x8 pf[KB][2];
-        vphase(t - 1, s_cur, pf, std::false_type{});
-        m2(std::integral_constant<int, SP>{}, pf);
-      }
-      pending = true;
-      m1(STc, s_cur);
-    }
-  };
-
-  // Tiles [0, t_plain) need no mask for any wave of the workgroup; they run
-  // unrolled over the LDS stages with the two groups offset. The rest
-  // (causal diagonal, ragged tail) run in step, masked, after group 1 has
-  // finished its pending tile.
+  // Every wave runs one tile behind itself: after barrier t it forms the
+  // scores of tile t (MFMA) while it exponentiates those of tile t-1 (VALU),
+  // then accumulates P*V of tile t-1, and the refill of tile t+PF is in
+  // flight. The scores alternate between two register sets; the loop is
+  // unrolled over UN tiles (a multiple of both the stage count and 2) so
+  // every stage offset and register set is a compile-time constant. The
+  // refill issued at barrier t targets stage (t+PF) % NSTAGE, last read by
+  // P*V of tile t-2 before that barrier.
+  f32x16 sb[2][KB];
+  f32x16 (&s_cur)[KB] = sb[0];
   int t_plain = Skv / BC;
   if (CAUSAL) t_plain = min(t_plain, max(0, (q0 + Skv - Sq + 1) / BC));
   t_plain = min(t_plain, nt);
-  const int t_main = t_plain - t_plain % NSTAGE;
-  auto run = [&](auto LAGc) {
-    bool pending = false;
-    for (int t = 0; t < t_main; t += NSTAGE)
-      static_for<NSTAGE>([&](auto STc) { tile(t + decltype(STc)::value, STc, LAGc, pending); });
-    if constexpr (decltype(LAGc)::value) {
-      if (pending) {  // tile t_main - 1 sits in stage NSTAGE - 1
-        bf16x8 pf[KB][2];
-        vphase(t_main - 1, s_cur, pf, std::false_type{});
-        m2(std::integral_constant<int, NSTAGE - 1>{}, pf);
-      }
-    }
-  };
-  if (lag) run(std::true_type{});
-  else run(std::false_type{});
-  int t = t_main;
-
-  // the remaining tiles run without the lag (both groups in step)
-  auto tile_step = [&](int tt, auto STc) {
-    constexpr int ST = decltype(STc)::value;
-    wait_vmcnt<0>();
+  // pipelined tiles: 0 .. t_main-1 with t_main = 1 + UN*k
+  const int t_main = t_plain >= 1 ? 1 + UN * ((t_plain - 1) / UN) : 0;
+  if (t_main > 0) {
+    wait_tile(0);
     wait_lgkmcnt0();
     barrier();
-    if (tt + 1 < nt) issue(tt + 1, std::integral_constant<int, (ST + 1) % NSTAGE>{});
+    if (PF < nt) issue(PF, std::integral_constant<int, PF % NSTAGE>{});
+    m1(std::integral_constant<int, 0>{}, sb[0]);
+    for (int t0 = 0; t0 + 1 < t_main; t0 += UN) {
+      static_for<UN>([&](auto Uc) {
+        constexpr int U = decltype(Uc)::value + 1;          // tile t0 + U
+        constexpr int ST = U % NSTAGE, SP = (U - 1) % NSTAGE;
+        constexpr int BN = U % 2, BP = (U - 1) % 2;
+        const int t = t0 + U;
+        wait_tile(t);
+        wait_lgkmcnt0();
+        barrier();
+        if (t + PF < nt) issue(t + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
+        vmax(t - 1, sb[BP], std::false_type{});
+        bf16x8 pf[KB][2];
+        vexp(sb[BP], pf);
+        m1(std::integral_constant<int, ST>{}, sb[BN]);
+        m2(std::integral_constant<int, SP>{}, pf);
+        // MFMAs of the scores alternate with the exponentials' VALU work,
+        // each group of K-fragment reads one step ahead; then P*V.
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2 * KB, 0);
+        static_for<KS * KB>([&](auto Ic) {
+          constexpr int i = decltype(Ic)::value;
+          constexpr int ahead = 2 * 2 * KB;  // reads issued before MFMA i
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, TATTN_VALU_PER_MFMA, 0);
+          if constexpr (i % (2 * KB) == 2 * KB - 1 && i + 1 + ahead <= KS * KB)
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
+        });
+        static_for<KB * 2>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, DB, 0);
+        });
+      });
+    }
+    // tile t_main - 1 (= UN*k: stage 0, set 0) still needs its softmax and P*V
+    bf16x8 pf[KB][2];
+    vphase(t_main - 1, sb[0], pf, std::false_type{});
+    m2(std::integral_constant<int, 0>{}, pf);
+  }
+
+  // the remaining tiles (causal diagonal, ragged tail) run masked, in order
+  auto tile_step = [&](int tt, auto STc) {
+    constexpr int ST = decltype(STc)::value;
+    wait_tile(tt);
+    wait_lgkmcnt0();
+    barrier();
+    if (tt + PF < nt) issue(tt + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
     if (CAUSAL && tt * BC > wave_kv_last) return;
     bf16x8 pf[KB][2];
     m1(STc, s_cur);
     vphase(tt, s_cur, pf, std::true_type{});
     m2(STc, pf);
   };
-  for (; t < nt; ++t) {
+  for (int t = t_main; t < nt; ++t) {
     const int st = t % NSTAGE;
-    if (st == 0) tile_step(t, std::integral_constant<int, 0>{});
-    else if (st == 1) tile_step(t, std::integral_constant<int, 1>{});
-    else tile_step(t, std::integral_constant<int, 2>{});
+    static_for<NSTAGE>([&](auto STc) {
+      if (st == decltype(STc)::value) tile_step(t, STc);
+    });
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
@@ -347,7 +390,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 template <int D, int NW, int BC, bool CAUSAL>
 static hipError_t launch_one(const MhaArgs& a, hipStream_t stream) {
   constexpr int BR = NW * 32;
-  constexpr int NSTAGE = 3;
+  constexpr int NSTAGE = TATTN_MHA_STAGES;
   constexpr size_t lds = 2 * (size_t)NSTAGE * BC * D * 2;
   auto kern = mha_fwd_bf16_kernel<D, NW, BC, NSTAGE, CAUSAL>;
   // Thread-safe one-time opt-in to more than the default dynamic LDS.
