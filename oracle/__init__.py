@@ -24,6 +24,11 @@ section):
   max m, running sum l, rescaled accumulator), in the order the study notes'
   "Online Softmax" subsection states it. It is used only to check that the
   recurrence reaches the two-pass result.
+* ``attention_masked`` / ``visible_keys`` -- the attention variants of
+  "TileLang study notes", section 5.1: grouped and single KV heads
+  (multi-query), a sliding key window around the query position, and a
+  block mask that decides which (query block, key block) pairs are
+  computed. Same definition as ``attention`` over each row's visible keys.
 * ``attention_partial`` / ``combine_partials`` -- per-key-range normalised
   partial outputs with their log-sum-exp, and the exact merge of such
   partials. The pages do not describe a split; this is the split-KV reading
@@ -37,9 +42,11 @@ independent library routine). Nothing is "parity unpinned".
 
 from .core import (  # noqa: F401
     attention,
+    attention_masked,
     attention_partial,
     combine_partials,
     mla_decode,
     mla_decode_rows,
     online_attention,
+    visible_keys,
 )

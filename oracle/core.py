@@ -171,6 +171,71 @@ def attention_partial(q, k, v, scale, key_lo, key_hi, causal=False):
     return out, lse
 
 
+def visible_keys(i, Sq, Skv, causal=False, window=0, block_row=None, block=64):
+    """Boolean vector over the Skv keys: which keys query row ``i`` sees.
+
+    Key j is visible when 0 <= j < Skv and, with off = Skv - Sq (the
+    bottom-right alignment used for the causal rule),
+      * causal: j <= i + off;
+      * window W > 0: i + off - W <= j < i + off + W. "TileLang study notes",
+        section 5.1 (local attention), makes a sliding window by running the
+        key loop over the positions from the query position minus the window
+        size up to (not including) the query position plus the window size;
+      * block mask: block_row[j // block] != 0, where ``block_row`` is the
+        mask row of the query block i // block. The same section makes sparse
+        attention by a mask matrix that decides which parts are computed;
+        the reading here is one bit per (query block, key block) pair.
+    """
+    j = np.arange(Skv)
+    vis = np.ones(Skv, dtype=bool)
+    pos = i + (Skv - Sq)
+    if causal:
+        vis &= j <= pos
+    if window > 0:
+        vis &= (j >= pos - window) & (j < pos + window)
+    if block_row is not None:
+        vis &= np.asarray(block_row)[j // block] != 0
+    return vis
+
+
+def attention_masked(q, k, v, scale, causal=False, window=0, block_mask=None, block=64, rows=None):
+    """Attention with grouped KV heads, a sliding window and a block mask.
+
+    The same definition as ``attention`` (S = scale*Q*K^T, softmax over each
+    row's visible keys, O = P*V, natural-log LSE), with the visible set of
+    ``visible_keys``. KV heads are shared by groups of query heads as in
+    ``attention`` (query head h reads KV head h // (H // Hkv)); with one KV
+    head this is the multi-query form of "TileLang study notes", section 5.1.
+    ``block_mask`` is [B, H, ceil(Sq/block), ceil(Skv/block)] (nonzero =
+    computed) or None. A row that sees no key gets O = 0 and LSE = -inf.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    scale = float(scale)
+    B, H, Sq, _ = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if H % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    group = H // Hkv
+    rows = np.arange(Sq) if rows is None else np.asarray(rows, dtype=np.int64)
+    Dv = v.shape[3]
+    out = np.zeros((B, H, rows.size, Dv))
+    lse = np.zeros((B, H, rows.size))
+    for b in range(B):
+        for h in range(H):
+            kh, vh = k[b, h // group], v[b, h // group]
+            s = scale * (q[b, h, rows] @ kh.T)
+            vis = np.stack([visible_keys(int(i), Sq, Skv, causal, window,
+                                         None if block_mask is None else block_mask[b, h, int(i) // block],
+                                         block) for i in rows]) if rows.size else np.zeros((0, Skv), bool)
+            masked = np.where(vis, s, _NEG_INF)
+            m = masked.max(axis=1) if Skv > 0 else np.full(rows.size, _NEG_INF)
+            safe_m = np.where(np.isfinite(m), m, 0.0)
+            p = np.where(vis, np.exp(masked - safe_m[:, None]), 0.0)
+            l = p.sum(axis=1)
+            out[b, h], lse[b, h] = _finish(p, m, l, vh)
+    return out, lse
+
+
 def combine_partials(o_parts, lse_parts):
     """Exact merge of per-range partials (the split-KV reading).
 

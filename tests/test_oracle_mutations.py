@@ -97,3 +97,51 @@ def test_missing_rescale_in_online_is_caught(monkeypatch, drop):
         return out, lse
     monkeypatch.setattr(oracle, "online_attention", online)
     assert _fails(pins.test_online_matches_two_pass, 7, False)
+
+
+def _patch_visible(monkeypatch, fn):
+    monkeypatch.setattr(oa, "visible_keys", fn)
+
+
+def test_window_upper_bound_off_by_one_is_caught(monkeypatch):
+    import tests.test_oracle_variants as vpins
+    real = oa.visible_keys
+
+    def vis(i, Sq, Skv, causal=False, window=0, block_row=None, block=64):
+        out = real(i, Sq, Skv, causal, window, block_row, block)
+        pos = i + Skv - Sq
+        if window > 0 and not causal and 0 <= pos + window < Skv:
+            out = out.copy()
+            out[pos + window] = True   # j <= pos + W instead of j < pos + W
+        return out
+    _patch_visible(monkeypatch, vis)
+    assert _fails(vpins.test_window_two_closed_form, 8, 8)
+
+
+def test_window_lower_bound_off_by_one_is_caught(monkeypatch):
+    import tests.test_oracle_variants as vpins
+    real = oa.visible_keys
+
+    def vis(i, Sq, Skv, causal=False, window=0, block_row=None, block=64):
+        out = real(i, Sq, Skv, causal, window, block_row, block)
+        pos = i + Skv - Sq
+        if window > 0 and 0 <= pos - window < Skv:
+            out = out.copy()
+            out[pos - window] = False  # j > pos - W instead of j >= pos - W
+        return out
+    _patch_visible(monkeypatch, vis)
+    assert _fails(vpins.test_window_is_attention_over_the_window_range, False, 3)
+
+
+def test_block_mask_transposed_is_caught(monkeypatch):
+    import tests.test_oracle_variants as vpins
+    real = oracle.attention_masked
+
+    def masked(q, k, v, scale, causal=False, window=0, block_mask=None, block=64, rows=None):
+        bm = None if block_mask is None else np.ascontiguousarray(
+            np.swapaxes(np.asarray(block_mask), 2, 3)[:, :, :block_mask.shape[2], :block_mask.shape[3]])
+        if bm is not None and bm.shape != np.asarray(block_mask).shape:
+            bm = np.resize(bm, np.asarray(block_mask).shape)
+        return real(q, k, v, scale, causal, window, bm, block, rows)
+    monkeypatch.setattr(oracle, "attention_masked", masked)
+    assert _fails(vpins.test_block_mask_one_block_per_row_is_that_range)
