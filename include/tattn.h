@@ -74,6 +74,37 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              void* stream);
 
 /*
+ * attn_fwd_ex -- attn_fwd with the attention variants of "TileLang study
+ * notes", section 5.1 (other attention variants): grouped or single KV heads
+ * (multi-query), a sliding key window (local attention) and a block mask
+ * (sparse attention). With Hkv == H, window == 0 and block_mask == NULL it
+ * computes exactly what attn_fwd computes.
+ *
+ *   k, v       device, bf16 [B, Hkv, Skv, D]; query head h reads KV head
+ *              h / (H / Hkv). Hkv >= 1 and H a multiple of Hkv, else
+ *              TATTN_ERR_INVALID_ARG.
+ *   window     0: no window. W > 0: row i sees only keys j with
+ *              pos - W <= j < pos + W, pos = i + (Skv - Sq) (the key loop of
+ *              the local-attention example runs from the query position minus
+ *              the window size to the query position plus it), intersected
+ *              with the causal rule when causal != 0. Negative: INVALID_ARG;
+ *              above 2^30: UNSUPPORTED.
+ *   block_mask NULL, or device uint8 [B, H, ceil(Sq/64), ceil(Skv/64)],
+ *              read only: the (64-row query block, 64-key block) pairs whose
+ *              byte is 0 are not computed (their scores count as -inf).
+ *              Any alignment.
+ *   everything else as attn_fwd (same layouts of q, o, lse; D 64 or 128).
+ *
+ * A row that sees no key (window, causal rule and mask together) gets O = 0
+ * and LSE = -inf. Grouped heads run at the speed of attn_fwd; with a window
+ * or a mask the kernel visits only the key tiles some row of a 256-row query
+ * tile can see.
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                int B, int H, int Hkv, int Sq, int Skv, int D, int causal, int window,
+                const uint8_t* block_mask, float scale, void* stream);
+
+/*
  * attn_fwd_f32 -- the same operation as attn_fwd with fp32 q, k, v and o
  * (fp32 arithmetic throughout). Same arguments, layouts, masking, edge
  * cases and status codes; q, k, v, o are fp32 and 16-byte aligned.

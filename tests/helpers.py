@@ -38,10 +38,28 @@ def parity_stats(o, lse, ro, rl):
             "rel_l2": float(rel), "max_lse": float(np.nan_to_num(dl, nan=np.inf).max()) if dl.size else 0.0}
 
 
+def bf16_half_ulp(x):
+    """Half a bf16 ulp at |x| (8 significant bits): the largest error of
+    rounding an exact value of that magnitude to bf16."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, np.exp2(e - 8), 0.0)
+
+
+def bf16_o_bound(ro):
+    """Per-element bound on |dO| for a bf16 output: 1e-2, plus, where the exact
+    value has |O| >= 2, the bf16 half-ulp of that value (rounding the exact
+    result to bf16 alone can reach 2^-9 |O|, above 1e-2 once |O| > 5.12)."""
+    ro = np.asarray(ro, dtype=np.float64)
+    return BF16_MAX_ABS_O + np.where(np.abs(ro) >= 2.0, bf16_half_ulp(ro), 0.0)
+
+
 def assert_bf16_parity(o, lse, ro, rl, what=""):
     st = parity_stats(o, lse, ro, rl)
     msg = f"{what}: {st}"
-    assert st["max_o"] <= BF16_MAX_ABS_O, msg
+    if st["max_o"] > BF16_MAX_ABS_O:  # only elements with |O| >= 2 may exceed 1e-2
+        excess = np.abs(o - ro) - bf16_o_bound(ro)
+        assert excess.max() <= 0, msg + f" (worst excess over the bf16 bound {excess.max():.3g})"
     assert st["mean_o"] <= BF16_MEAN_ABS_O, msg
     assert st["max_lse"] <= BF16_MAX_ABS_LSE, msg
     assert st["rel_l2"] <= BF16_REL_L2_O, msg

@@ -63,3 +63,27 @@ def test_cpu_baseline_budget_is_bounded(monkeypatch):
     assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s"
     assert out["value"] > 0 and out["cores"] >= 1
     assert np.isfinite(out["value"])
+
+
+def test_bf16_output_bound():
+    from tests.helpers import bf16_half_ulp, bf16_o_bound
+    # half-ulps of bf16 (8 significant bits) at a few magnitudes
+    assert bf16_half_ulp(1.0) == 2.0 ** -8
+    assert bf16_half_ulp(3.0) == 2.0 ** -7
+    assert bf16_half_ulp(-5.0) == 2.0 ** -6
+    assert bf16_half_ulp(0.0) == 0.0
+    # below |O| = 2 the bound is exactly 1e-2
+    assert bf16_o_bound(1.99) == 1e-2 and bf16_o_bound(-0.3) == 1e-2
+    assert bf16_o_bound(4.5) == 1e-2 + 2.0 ** -6
+
+
+@pytest.mark.parametrize("Sq,Skv,causal,W", [(7, 9, True, 2), (9, 7, False, 3), (130, 70, True, 0), (130, 200, False, 50)])
+def test_visible_pairs_brute_force(Sq, Skv, causal, W):
+    from tiled_attention_12_amd.workloads import visible_pairs
+    rng = np.random.default_rng(Sq + Skv)
+    m = (rng.random((-(-Sq // 64), -(-Skv // 64))) < 0.5).astype(np.uint8)
+    for mask in (None, m):
+        bf = sum(1 for i in range(Sq) for j in range(Skv)
+                 if (not causal or j <= i + Skv - Sq) and (W == 0 or i + Skv - Sq - W <= j < i + Skv - Sq + W)
+                 and (mask is None or mask[i // 64, j // 64]))
+        assert visible_pairs(Sq, Skv, causal, W, mask) == bf

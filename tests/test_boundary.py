@@ -20,7 +20,7 @@ def _header_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert _header_symbols() == ["attn_fwd", "attn_fwd_f32", "mla_decode", "tattn_status_str"]
+    assert _header_symbols() == ["attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "tattn_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib_path):
@@ -74,6 +74,23 @@ def test_mha_argument_validation(L, fn):
     assert st in (OK, HIP)
 
 
+def test_mha_ex_argument_validation(L):
+    def call(q=16, k=16, v=16, o=16, lse=16, B=1, H=4, Hkv=2, Sq=8, Skv=8, D=128, causal=0, window=0,
+             mask=None, scale=0.1):
+        return L.attn_fwd_ex(q, k, v, o, lse, B, H, Hkv, Sq, Skv, D, causal, window, mask, F(scale), None)
+    assert call(Hkv=0) == INVALID
+    assert call(Hkv=-1) == INVALID
+    assert call(Hkv=3) == INVALID          # 4 query heads do not split into groups of 3 KV heads
+    assert call(window=-1) == INVALID
+    assert call(window=(1 << 30) + 1) == UNSUP
+    assert call(q=None) == INVALID
+    assert call(scale=0.0) == INVALID
+    assert call(D=80) == UNSUP
+    assert call(k=40) == ALIGN
+    assert call(B=0, q=None, k=None, v=None, o=None, lse=None) == OK
+    assert call(H=0, Hkv=0, q=None) == OK
+
+
 def test_mla_argument_validation(L):
     def call(q=16, qpe=16, kv=16, kpe=16, o=16, lse=16, B=2, H=128, ind=16, scale=0.05):
         return L.mla_decode(q, qpe, kv, kpe, o, lse, B, H, ind, F(scale), None)
@@ -98,12 +115,13 @@ def test_valid_request_without_gpu_is_a_hip_error(lib_path):
         "r1=L.attn_fwd(16,16,16,16,16,1,1,8,8,128,0,F(0.1),None);"
         "r2=L.attn_fwd_f32(16,16,16,16,16,1,1,8,8,64,1,F(0.1),None);"
         "r3=L.mla_decode(16,16,16,16,16,16,2,128,16,F(0.1),None);"
-        "print(r1,r2,r3)"
+        "r4=L.attn_fwd_ex(16,16,16,16,16,1,4,1,8,8,128,1,3,None,F(0.1),None);"
+        "print(r1,r2,r3,r4)"
     )
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1")
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
     assert out.returncode == 0, out.stderr
-    assert out.stdout.split() == [str(HIP)] * 3
+    assert out.stdout.split() == [str(HIP)] * 4
 
 
 def test_status_strings_cover_every_code(L):

@@ -19,7 +19,7 @@ TATTN_ERR_ALIGN = -3
 TATTN_ERR_OOM = -4
 TATTN_ERR_HIP = -5
 
-EXPORTED = ("attn_fwd", "attn_fwd_f32", "mla_decode", "tattn_status_str")
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "tattn_status_str")
 
 
 class TattnError(RuntimeError):
@@ -41,6 +41,8 @@ def _load():
     lib.attn_fwd.restype = i32
     lib.attn_fwd_f32.argtypes = mha
     lib.attn_fwd_f32.restype = i32
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, f32, vp]
+    lib.attn_fwd_ex.restype = i32
     lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, f32, vp]
     lib.mla_decode.restype = i32
     lib.tattn_status_str.argtypes = [i32]
@@ -116,6 +118,42 @@ def _mha(fn_name, q, k, v, causal, scale, out, lse, stream, dtype):
 def attn_fwd(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):
     """bf16 multi-head attention forward: returns (O bf16 [B,H,Sq,D], LSE fp32 [B,H,Sq])."""
     return _mha("attn_fwd", q, k, v, causal, scale, out, lse, stream, _torch().bfloat16)
+
+
+def attn_fwd_ex(q, k, v, causal=False, scale=None, window=0, block_mask=None, out=None, lse=None,
+                stream=None):
+    """bf16 attention with grouped KV heads (k, v [B, Hkv, Skv, D]), an optional
+    key window (0: none) and an optional uint8 block mask [B, H, ceil(Sq/64),
+    ceil(Skv/64)] on the device. Returns (O bf16 [B,H,Sq,D], LSE fp32 [B,H,Sq])."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    Hkv, Skv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Skv, D) or tuple(v.shape) != (B, Hkv, Skv, D):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    dev = q.device
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_dev(n, t, torch.bfloat16, dev)
+    if block_mask is not None:
+        _check_dev("block_mask", block_mask, torch.uint8, dev)
+        if tuple(block_mask.shape) != (B, H, -(-Sq // 64), -(-Skv // 64)):
+            raise ValueError("block_mask must be uint8 [B, H, ceil(Sq/64), ceil(Skv/64)]")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    _check_dev("out", out, torch.bfloat16, dev)
+    _check_dev("lse", lse, torch.float32, dev)
+    if tuple(out.shape) != (B, H, Sq, D) or tuple(lse.shape) != (B, H, Sq):
+        raise ValueError("out/lse have the wrong shape")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    rc = _LIB.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Sq, Skv, D,
+                          int(bool(causal)), int(window), _ptr(block_mask), ctypes.c_float(scale),
+                          _stream_ptr(dev, stream))
+    if rc != TATTN_OK:
+        raise TattnError(rc, "attn_fwd_ex")
+    return out, lse
 
 
 def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None, stream=None):

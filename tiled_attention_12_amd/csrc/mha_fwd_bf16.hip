@@ -62,9 +62,18 @@ struct MhaArgs {
   int n_qtiles;
   float c;    // scale * log2(e)
   int remap;  // n_bh % 8 == 0: XCD-grouped order
+  int H;      // query heads
+  int group;  // query heads per KV head
+  int window; // key window half-width (0: none)
+  const uint8_t* bmask;  // [B, H, nqb, nkb] per 64x64 block, or null
+  int nqb, nkb;
 };
 
-template <int D, int NW, int BC, int NSTAGE, bool CAUSAL>
+// Block size of the block mask: 64 query rows x 64 keys (one key tile; each
+// wave's 32 rows lie inside one query block).
+constexpr int kMaskBlock = 64;
+
+template <int D, int NW, int BC, int NSTAGE, bool CAUSAL, bool EXT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void mha_fwd_bf16_kernel(MhaArgs a) {
   constexpr int BR = NW * 32;      // query rows per workgroup (32 per wave)
   constexpr int CPR = D / 8;       // 16-byte chunks per row
@@ -111,8 +120,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int q0 = qt * BR;
   const int wrow0 = q0 + wave * 32;
   const uint16_t* qp = a.q + (size_t)bh * Sq * D;
-  const char* kp = (const char*)(a.k + (size_t)bh * Skv * D);
-  const char* vp = (const char*)(a.v + (size_t)bh * Skv * D);
+  // query head h of batch b reads KV head h / group
+  const int bq = bh / a.H, hq = bh - bq * a.H;
+  const size_t kvh = (size_t)bq * (a.H / a.group) + hq / a.group;
+  const char* kp = (const char*)(a.k + kvh * Skv * D);
+  const char* vp = (const char*)(a.v + kvh * Skv * D);
   const float c = a.c;
 
   int kv_end = Skv;
@@ -160,9 +172,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
   };
 
-  static_for<PF>([&](auto Ic) {
-    if (decltype(Ic)::value < nt) issue(decltype(Ic)::value, Ic);
-  });
+  if constexpr (!EXT) {
+    static_for<PF>([&](auto Ic) {
+      if (decltype(Ic)::value < nt) issue(decltype(Ic)::value, Ic);
+    });
+  }
   // wait until this wave's loads of tile t have landed (tiles up to
   // t + PF - 1 may still be in flight)
   auto wait_tile = [&](int t) {
@@ -225,12 +239,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto vmax = [&](int t, f32x16 (&s)[KB], auto MASKEDc) {
     const int kv0 = t * BC;
     if constexpr (decltype(MASKEDc)::value) {
-      const int lim = CAUSAL ? min(Skv - 1, wrow0 + col + Skv - Sq) : Skv - 1;
+      // key j is visible to this lane's row when lo <= j <= lim
+      const int pos = wrow0 + col + Skv - Sq;
+      int lim = CAUSAL ? min(Skv - 1, pos) : Skv - 1;
+      int lo = 0;
+      if constexpr (EXT) {
+        if (a.window > 0) {
+          lim = min(lim, pos + a.window - 1);
+          lo = pos - a.window;
+        }
+      }
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (kv0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3) > lim) s[kb][i] = -INFINITY;
+        for (int i = 0; i < 16; ++i) {
+          const int j = kv0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+          if (j > lim || j < lo) s[kb][i] = -INFINITY;
+        }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -287,83 +312,150 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     });
   };
 
-  // Every wave runs one tile behind itself: after barrier t it forms the
-  // scores of tile t (MFMA) while it exponentiates those of tile t-1 (VALU),
-  // then accumulates P*V of tile t-1, and the refill of tile t+PF is in
-  // flight. The scores alternate between two register sets; the loop is
-  // unrolled over UN tiles (a multiple of both the stage count and 2) so
-  // every stage offset and register set is a compile-time constant. The
-  // refill issued at barrier t targets stage (t+PF) % NSTAGE, last read by
-  // P*V of tile t-2 before that barrier.
-  f32x16 sb[2][KB];
-  f32x16 (&s_cur)[KB] = sb[0];
-  int t_plain = Skv / BC;
-  if (CAUSAL) t_plain = min(t_plain, max(0, (q0 + Skv - Sq + 1) / BC));
-  t_plain = min(t_plain, nt);
-  // pipelined tiles: 0 .. t_main-1 with t_main = 1 + UN*k
-  const int t_main = t_plain >= 1 ? 1 + UN * ((t_plain - 1) / UN) : 0;
-  if (t_main > 0) {
-    wait_tile(0);
-    wait_lgkmcnt0();
-    barrier();
-    if (PF < nt) issue(PF, std::integral_constant<int, PF % NSTAGE>{});
-    m1(std::integral_constant<int, 0>{}, sb[0]);
-    for (int t0 = 0; t0 + 1 < t_main; t0 += UN) {
-      static_for<UN>([&](auto Uc) {
-        constexpr int U = decltype(Uc)::value + 1;          // tile t0 + U
-        constexpr int ST = U % NSTAGE, SP = (U - 1) % NSTAGE;
-        constexpr int BN = U % 2, BP = (U - 1) % 2;
-        const int t = t0 + U;
-        wait_tile(t);
+  if constexpr (EXT) {
+    // Sliding window and/or block mask: the workgroup walks only the key
+    // tiles that some of its rows can see and that the block mask keeps,
+    // one tile in flight; a wave whose own rows see nothing of a tile (or
+    // whose query block masks it) skips that tile's arithmetic. Every such
+    // tile is masked per element (window edges, causal diagonal, tail).
+    const int W = a.window;
+    const int off = Skv - Sq;
+    const int last_row = min(q0 + BR, Sq) - 1;
+    int lo = 0, hi = Skv;
+    if (CAUSAL) hi = min(hi, last_row + off + 1);
+    if (W > 0) {
+      lo = max(0, q0 + off - W);
+      hi = min(hi, last_row + off + W);
+    }
+    const int t_first = lo / BC;
+    const int t_end = hi > lo ? (hi + BC - 1) / BC : t_first;
+    const int wlast = min(wrow0 + 31, Sq - 1);
+    int wlo = 0, whi = Skv;
+    if (CAUSAL) whi = min(whi, wlast + off + 1);
+    if (W > 0) {
+      wlo = max(0, wrow0 + off - W);
+      whi = min(whi, wlast + off + W);
+    }
+    const bool wave_rows = wrow0 < Sq;
+    const uint8_t* mrow = a.bmask ? a.bmask + (size_t)bh * a.nqb * a.nkb : nullptr;
+    const int qb_first = q0 / kMaskBlock, qb_last = last_row / kMaskBlock, qb_w = wrow0 / kMaskBlock;
+    auto active = [&](int t) {
+      if (!mrow) return true;
+      int any = 0;
+      for (int qb = qb_first; qb <= qb_last; ++qb) any |= mrow[qb * a.nkb + t];
+      return any != 0;
+    };
+    auto next_active = [&](int t) {
+      do { ++t; } while (t < t_end && !active(t));
+      return t;
+    };
+    f32x16 sx[KB];
+    int cur = t_first;
+    if (cur < t_end && !active(cur)) cur = next_active(cur);
+    if (cur < t_end) issue(cur, std::integral_constant<int, 0>{});
+    for (int cnt = 0; cur < t_end; ++cnt) {
+      // mask bytes are read before the next refill is issued, so waiting for
+      // them never waits for that refill
+      const int nxt = next_active(cur);
+      const bool wact = wave_rows && cur * BC < whi && (cur + 1) * BC > wlo &&
+                        (!mrow || mrow[qb_w * a.nkb + cur] != 0);
+      const int st = cnt % NSTAGE;
+      static_for<NSTAGE>([&](auto STc) {
+        constexpr int ST = decltype(STc)::value;
+        if (st != ST) return;
+        wait_vmcnt<0>();
         wait_lgkmcnt0();
         barrier();
-        if (t + PF < nt) issue(t + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
-        vmax(t - 1, sb[BP], std::false_type{});
-        bf16x8 pf[KB][2];
-        vexp(sb[BP], pf);
-        m1(std::integral_constant<int, ST>{}, sb[BN]);
-        m2(std::integral_constant<int, SP>{}, pf);
-        // MFMAs of the scores alternate with the exponentials' VALU work,
-        // each group of K-fragment reads one step ahead; then P*V.
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2 * KB, 0);
-        static_for<KS * KB>([&](auto Ic) {
-          constexpr int i = decltype(Ic)::value;
-          constexpr int ahead = 2 * 2 * KB;  // reads issued before MFMA i
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, TATTN_VALU_PER_MFMA, 0);
-          if constexpr (i % (2 * KB) == 2 * KB - 1 && i + 1 + ahead <= KS * KB)
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
+        if (nxt < t_end) issue(nxt, std::integral_constant<int, (ST + 1) % NSTAGE>{});
+        if (wact) {
+          bf16x8 pf[KB][2];
+          m1(STc, sx);
+          vphase(cur, sx, pf, std::true_type{});
+          m2(STc, pf);
+        }
+      });
+      cur = nxt;
+    }
+  } else {
+    // Every wave runs one tile behind itself: after barrier t it forms the
+    // scores of tile t (MFMA) while it exponentiates those of tile t-1 (VALU),
+    // then accumulates P*V of tile t-1, and the refill of tile t+PF is in
+    // flight. The scores alternate between two register sets; the loop is
+    // unrolled over UN tiles (a multiple of both the stage count and 2) so
+    // every stage offset and register set is a compile-time constant. The
+    // refill issued at barrier t targets stage (t+PF) % NSTAGE, last read by
+    // P*V of tile t-2 before that barrier.
+    f32x16 sb[2][KB];
+    f32x16 (&s_cur)[KB] = sb[0];
+    int t_plain = Skv / BC;
+    if (CAUSAL) t_plain = min(t_plain, max(0, (q0 + Skv - Sq + 1) / BC));
+    t_plain = min(t_plain, nt);
+    // pipelined tiles: 0 .. t_main-1 with t_main = 1 + UN*k
+    const int t_main = t_plain >= 1 ? 1 + UN * ((t_plain - 1) / UN) : 0;
+    if (t_main > 0) {
+      wait_tile(0);
+      wait_lgkmcnt0();
+      barrier();
+      if (PF < nt) issue(PF, std::integral_constant<int, PF % NSTAGE>{});
+      m1(std::integral_constant<int, 0>{}, sb[0]);
+      for (int t0 = 0; t0 + 1 < t_main; t0 += UN) {
+        static_for<UN>([&](auto Uc) {
+          constexpr int U = decltype(Uc)::value + 1;          // tile t0 + U
+          constexpr int ST = U % NSTAGE, SP = (U - 1) % NSTAGE;
+          constexpr int BN = U % 2, BP = (U - 1) % 2;
+          const int t = t0 + U;
+          wait_tile(t);
+          wait_lgkmcnt0();
+          barrier();
+          if (t + PF < nt) issue(t + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
+          vmax(t - 1, sb[BP], std::false_type{});
+          bf16x8 pf[KB][2];
+          vexp(sb[BP], pf);
+          m1(std::integral_constant<int, ST>{}, sb[BN]);
+          m2(std::integral_constant<int, SP>{}, pf);
+          // MFMAs of the scores alternate with the exponentials' VALU work,
+          // each group of K-fragment reads one step ahead; then P*V.
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2 * KB, 0);
+          static_for<KS * KB>([&](auto Ic) {
+            constexpr int i = decltype(Ic)::value;
+            constexpr int ahead = 2 * 2 * KB;  // reads issued before MFMA i
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, TATTN_VALU_PER_MFMA, 0);
+            if constexpr (i % (2 * KB) == 2 * KB - 1 && i + 1 + ahead <= KS * KB)
+              __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
+          });
+          static_for<KB * 2>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, DB, 0);
+          });
         });
-        static_for<KB * 2>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, DB, 0);
-        });
+      }
+      // tile t_main - 1 (= UN*k: stage 0, set 0) still needs its softmax and P*V
+      bf16x8 pf[KB][2];
+      vphase(t_main - 1, sb[0], pf, std::false_type{});
+      m2(std::integral_constant<int, 0>{}, pf);
+    }
+
+    // the remaining tiles (causal diagonal, ragged tail) run masked, in order
+    auto tile_step = [&](int tt, auto STc) {
+      constexpr int ST = decltype(STc)::value;
+      wait_tile(tt);
+      wait_lgkmcnt0();
+      barrier();
+      if (tt + PF < nt) issue(tt + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
+      if (CAUSAL && tt * BC > wave_kv_last) return;
+      bf16x8 pf[KB][2];
+      m1(STc, s_cur);
+      vphase(tt, s_cur, pf, std::true_type{});
+      m2(STc, pf);
+    };
+    for (int t = t_main; t < nt; ++t) {
+      const int st = t % NSTAGE;
+      static_for<NSTAGE>([&](auto STc) {
+        if (st == decltype(STc)::value) tile_step(t, STc);
       });
     }
-    // tile t_main - 1 (= UN*k: stage 0, set 0) still needs its softmax and P*V
-    bf16x8 pf[KB][2];
-    vphase(t_main - 1, sb[0], pf, std::false_type{});
-    m2(std::integral_constant<int, 0>{}, pf);
-  }
 
-  // the remaining tiles (causal diagonal, ragged tail) run masked, in order
-  auto tile_step = [&](int tt, auto STc) {
-    constexpr int ST = decltype(STc)::value;
-    wait_tile(tt);
-    wait_lgkmcnt0();
-    barrier();
-    if (tt + PF < nt) issue(tt + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
-    if (CAUSAL && tt * BC > wave_kv_last) return;
-    bf16x8 pf[KB][2];
-    m1(STc, s_cur);
-    vphase(tt, s_cur, pf, std::true_type{});
-    m2(STc, pf);
-  };
-  for (int t = t_main; t < nt; ++t) {
-    const int st = t % NSTAGE;
-    static_for<NSTAGE>([&](auto STc) {
-      if (st == decltype(STc)::value) tile_step(t, STc);
-    });
   }
 
   // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
@@ -387,12 +479,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-template <int D, int NW, int BC, bool CAUSAL>
+template <int D, int NW, int BC, bool CAUSAL, bool EXT>
 static hipError_t launch_one(const MhaArgs& a, hipStream_t stream) {
   constexpr int BR = NW * 32;
   constexpr int NSTAGE = TATTN_MHA_STAGES;
   constexpr size_t lds = 2 * (size_t)NSTAGE * BC * D * 2;
-  auto kern = mha_fwd_bf16_kernel<D, NW, BC, NSTAGE, CAUSAL>;
+  auto kern = mha_fwd_bf16_kernel<D, NW, BC, NSTAGE, CAUSAL, EXT>;
   // Thread-safe one-time opt-in to more than the default dynamic LDS.
   static const hipError_t attr_err =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -407,8 +499,8 @@ static hipError_t launch_one(const MhaArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                               int B, int H, int Sq, int Skv, int D, bool causal, float scale,
-                               hipStream_t stream) {
+                               int B, int H, int Hkv, int Sq, int Skv, int D, bool causal, int window,
+                               const uint8_t* block_mask, float scale, hipStream_t stream) {
   MhaArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -419,8 +511,19 @@ hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void
   a.Skv = Skv;
   a.n_bh = B * H;
   a.c = scale * kLog2e;
-  if (D == 128) return causal ? launch_one<128, 8, 64, true>(a, stream) : launch_one<128, 8, 64, false>(a, stream);
-  return causal ? launch_one<64, 8, 64, true>(a, stream) : launch_one<64, 8, 64, false>(a, stream);
+  a.H = H;
+  a.group = H / Hkv;
+  a.window = window;
+  a.bmask = block_mask;
+  a.nqb = (Sq + kMaskBlock - 1) / kMaskBlock;
+  a.nkb = (Skv + kMaskBlock - 1) / kMaskBlock;
+  const bool ext = window > 0 || block_mask != nullptr;
+  if (ext) {
+    if (D == 128) return causal ? launch_one<128, 8, 64, true, true>(a, stream) : launch_one<128, 8, 64, false, true>(a, stream);
+    return causal ? launch_one<64, 8, 64, true, true>(a, stream) : launch_one<64, 8, 64, false, true>(a, stream);
+  }
+  if (D == 128) return causal ? launch_one<128, 8, 64, true, false>(a, stream) : launch_one<128, 8, 64, false, false>(a, stream);
+  return causal ? launch_one<64, 8, 64, true, false>(a, stream) : launch_one<64, 8, 64, false, false>(a, stream);
 }
 
 }  // namespace tattn

@@ -81,8 +81,23 @@ TATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, flo
   int st = check_mha(q, k, v, o, lse, B, H, Sq, Skv, D, causal, scale, &nothing);
   if (st != TATTN_OK || nothing) return st;
   if ((st = have_device()) != TATTN_OK) return st;
-  return status_of(tattn::launch_mha_fwd_bf16(q, k, v, o, lse, B, H, Sq, Skv, D, causal != 0, scale,
-                                              (hipStream_t)stream));
+  return status_of(tattn::launch_mha_fwd_bf16(q, k, v, o, lse, B, H, H, Sq, Skv, D, causal != 0, 0, nullptr,
+                                              scale, (hipStream_t)stream));
+}
+
+TATTN_API int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                          int Hkv, int Sq, int Skv, int D, int causal, int window, const uint8_t* block_mask,
+                          float scale, void* stream) {
+  if (Hkv < 1 && !(B == 0 || H == 0)) return TATTN_ERR_INVALID_ARG;
+  if (Hkv > 0 && H % Hkv != 0) return TATTN_ERR_INVALID_ARG;
+  if (window < 0) return TATTN_ERR_INVALID_ARG;
+  if (window > kMaxSeq) return TATTN_ERR_UNSUPPORTED;
+  bool nothing = false;
+  int st = check_mha(q, k, v, o, lse, B, H, Sq, Skv, D, causal, scale, &nothing);
+  if (st != TATTN_OK || nothing) return st;
+  if ((st = have_device()) != TATTN_OK) return st;
+  return status_of(tattn::launch_mha_fwd_bf16(q, k, v, o, lse, B, H, Hkv, Sq, Skv, D, causal != 0, window,
+                                              block_mask, scale, (hipStream_t)stream));
 }
 
 TATTN_API int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,

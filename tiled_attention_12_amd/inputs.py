@@ -94,3 +94,12 @@ def mla_inputs(B, H, seed, kv_len=None, kv_len_range=None, sigma=0.3, Dl=512, Dr
     k_pe = f32_to_bf16_bits(_draw(rng, (n, Dr), sigma))
     return {"q": q, "q_pe": q_pe, "kv": kv, "k_pe": k_pe,
             "indptr": indptr.astype(np.int32), "lens": lens}
+
+
+def block_mask(B, H, Sq, Skv, density, seed, block=64):
+    """uint8 [B, H, ceil(Sq/block), ceil(Skv/block)]: each (query block, key
+    block) pair kept (1) independently with probability ``density``."""
+    rng = np.random.default_rng(seed)
+    shape = (B, H, -(-Sq // block), -(-Skv // block))
+    return (rng.random(shape) < density).astype(np.uint8)
+

@@ -24,6 +24,14 @@ WORKLOADS = {
                             scale=F32_SCALE_576, seed=1004),
     "mla_decode_ragged_bf16": dict(kind="mla", B=128, H=128, kv_len_range=(1024, 16384),
                                    sigma=0.3, scale=F32_SCALE_576, seed=1005),
+    # attention variants (grouped KV heads, sliding window, block mask)
+    "mha_gqa_bf16": dict(kind="mha", dtype="bf16", B=4, H=16, Hkv=4, Sq=2048, Skv=2048, D=128,
+                         causal=(False, True), sigma=1.0, scale=F32_SCALE_128, seed=1006),
+    "mha_window_bf16": dict(kind="mha", dtype="bf16", B=4, H=16, Sq=8192, Skv=8192, D=128,
+                            causal=(True,), window=256, sigma=1.0, scale=F32_SCALE_128, seed=1007),
+    "mha_blocksparse_bf16": dict(kind="mha", dtype="bf16", B=4, H=16, Sq=4096, Skv=4096, D=128,
+                                 causal=(False,), density=0.5, sigma=1.0, scale=F32_SCALE_128,
+                                 seed=1008),
 }
 
 
@@ -35,6 +43,30 @@ def mha_flops(B, H, Sq, Skv, D, causal, Dv=None):
     else:
         pairs = Sq * Skv
     return 2 * B * H * pairs * (D + Dv)
+
+
+def visible_pairs(Sq, Skv, causal=False, window=0, mask=None, block=64):
+    """Number of visible (query, key) pairs: per row the key interval from the
+    causal rule and the window, intersected with the kept mask blocks.
+    ``mask`` is one (query block, key block) mask [nqb, nkb] or None."""
+    i = np.arange(Sq, dtype=np.int64)
+    pos = i + (Skv - Sq)
+    lo = np.zeros(Sq, dtype=np.int64)
+    hi = np.full(Sq, Skv, dtype=np.int64)
+    if causal:
+        hi = np.minimum(hi, pos + 1)
+    if window > 0:
+        lo = np.maximum(lo, pos - window)
+        hi = np.minimum(hi, pos + window)
+    hi = np.maximum(hi, lo)
+    if mask is None:
+        return int((hi - lo).sum())
+    nkb = -(-Skv // block)
+    kb0 = np.arange(nkb, dtype=np.int64) * block
+    kb1 = np.minimum(kb0 + block, Skv)
+    inter = np.clip(np.minimum(hi[:, None], kb1[None, :]) - np.maximum(lo[:, None], kb0[None, :]), 0, None)
+    keep = np.asarray(mask)[i // block].astype(np.int64)
+    return int((inter * keep).sum())
 
 
 def mha_bytes(B, H, Sq, Skv, D, elem, Hkv=None, Dv=None):
