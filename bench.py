@@ -2,7 +2,8 @@
 
 One step = one pass of the prefill hot path over the headline workload
 (bf16 MHA B=4, H=16, Sq=Skv=2048, D=128), run once non-causal and once
-causal. The long causal prefill (B=1, H=32, S=16384) and the two MLA decode
+causal. The long causal prefill (B=1, H=32, S=16384), the attention variants
+(grouped KV heads, sliding window, block mask) and the two MLA decode
 workloads are measured in the same run and reported under "workloads".
 Inputs are seeded synthetic draws, resident in HBM before timing; each
 workload rotates three input copies so consecutive launches read cold data.
@@ -34,8 +35,8 @@ N_COPIES = 3
 # were taken on; once those files change the field is reported as null.
 TRAFFIC_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip",
                    "tiled_attention_12_amd/csrc/device_common.h")
-TRAFFIC = {"sources_sha256": "a93373d9869721eb1f86d7e29472125702cbfce91fcd41558ac8f7e609c2aa14",
-           "fetch_kib": 82104.0, "fetch_factor": 2.0, "write_kib": 33282.0, "write_factor": 1.0}
+TRAFFIC = {"sources_sha256": "a150fdb402904906fd349762305a5083df68dbc6f263d9f0d88c845eaca316d7",
+           "fetch_kib": 82105.0, "fetch_factor": 2.0, "write_kib": 33281.0, "write_factor": 1.0}
 
 
 def _traffic_bytes():
@@ -295,6 +296,36 @@ def main():
                                              "frac_mfma_peak": f3 / (mean3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
         del sets3, o3, l3
 
+        from tiled_attention_12_amd import inputs
+        from tiled_attention_12_amd.workloads import WORKLOADS, visible_pairs
+        for name in ("mha_gqa_bf16", "mha_window_bf16", "mha_blocksparse_bf16"):
+            _log(f"bench: {name}")
+            wv = WORKLOADS[name]
+            xv = inputs.mha_inputs(wv["B"], wv["H"], wv["Sq"], wv["Skv"], wv["D"], seed=wv["seed"],
+                                   sigma=wv["sigma"], Hkv=wv.get("Hkv"))
+            setsv = _copies(xv, dev)
+            window = wv.get("window", 0)
+            mask_np = mask_dev = None
+            if "density" in wv:
+                mask_np = inputs.block_mask(wv["B"], wv["H"], wv["Sq"], wv["Skv"], wv["density"], seed=wv["seed"] + 100)
+                mask_dev = _to_dev(mask_np, dev)
+            ov, lv = ta.attn_fwd_ex(setsv[0]["q"], setsv[0]["k"], setsv[0]["v"], scale=wv["scale"])
+            for causal in wv["causal"]:
+                fn = (lambda s, c=causal: ta.attn_fwd_ex(s["q"], s["k"], s["v"], causal=c, scale=wv["scale"],
+                                                         window=window, block_mask=mask_dev, out=ov, lse=lv))
+                mean_v, med_v, min_v = _time_launches(fn, setsv, 2, 10)
+                if mask_np is None:
+                    pairs = wv["B"] * wv["H"] * visible_pairs(wv["Sq"], wv["Skv"], causal, window)
+                else:
+                    pairs = sum(visible_pairs(wv["Sq"], wv["Skv"], causal, window, mask_np[b, h])
+                                for b in range(wv["B"]) for h in range(wv["H"]))
+                fv = 2 * pairs * 2 * wv["D"]
+                key = f"{name}_{'causal' if causal else 'noncausal'}"
+                workloads[key] = {"ms": mean_v, "ms_median": med_v, "ms_min": min_v, "visible_pairs": pairs,
+                                  "tflops": fv / (mean_v * 1e-3) / 1e12,
+                                  "frac_mfma_peak": fv / (mean_v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+            del setsv, ov, lv, mask_dev
+
         for name in ("mla_decode_bf16", "mla_decode_ragged_bf16"):
             _log(f"bench: {name}")
             wm, setsm, total = _mla_workload(ta, dev, name)
@@ -331,7 +362,7 @@ def main():
                    "global_batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": _traffic_bytes(),
-                     "kernel": "mha_fwd_bf16_kernel<128, 8, 64, 3, false> (non-causal)",
+                     "kernel": "mha_fwd_bf16_kernel<128, 8, 64, 3, false, false> (non-causal)",
                      "alg_flops_per_launch": f_nc, "alg_bytes_per_launch": nbytes},
         "workloads": workloads,
     }
