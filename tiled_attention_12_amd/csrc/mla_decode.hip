@@ -10,7 +10,10 @@
 // as both keys and values.
 //
 // Three kernels:
-//  1. plan:    tile_ptr[b] = number of 32-key tiles in batches before b.
+//  1. plan:    tile_ptr[b] = number of 32-key tiles in batches before b (a
+//              separate launch for many batches; below kFusedPlanMax batches
+//              every split workgroup forms it in LDS and workgroup 0 writes it
+//              out for the merge).
 //  2. split:   one persistent workgroup per compute unit takes an equal,
 //              contiguous slice of the packed tile range (a slice may span
 //              batches) and, for each batch it touches, writes the
@@ -42,6 +45,9 @@ constexpr int kBK = 32;      // keys per tile
 constexpr int kTileL = kBK * kDl * 2;
 constexpr int kTileR = kBK * kDr * 2;
 constexpr int kStage = kTileL + kTileR;
+// Up to this many batches the split kernel forms the tile prefix itself (in
+// LDS beside the ring) instead of a separate plan launch.
+constexpr int kFusedPlanMax = 1024;
 
 struct MlaArgs {
   const uint16_t* q;
@@ -159,7 +165,7 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a, int P) {
   if ((threadIdx.x & 31) == 0) a.lse[(size_t)b * H + h] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
 }
 
-template <int NW, int NSTAGE>
+template <int NW, int NSTAGE, bool FUSE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_split_kernel(MlaArgs a) {
   constexpr int KS = (kDl + kDr) / 16;          // 36 k-steps of the score product
@@ -202,8 +208,44 @@ void mla_split_kernel(MlaArgs a) {
     }
   }
 
+  // Tile prefix: tile_ptr[b] = tiles of batches before b. With fuse_plan the
+  // workgroup forms it in LDS (and workgroup 0 also writes it out for the
+  // merge kernel); otherwise the plan kernel has written it.
+  typedef __attribute__((address_space(3))) int lds_int;
+  lds_int* tp_lds = (lds_int*)(uintptr_t)lds_addr(smem + NSTAGE * kStage);
+  if constexpr (FUSE) {
+    const int B = a.B, nthr = NW * 64, t = threadIdx.x;
+    const int per = (B + nthr - 1) / nthr;
+    const int b0 = min(B, t * per), b1 = min(B, b0 + per);
+    int local = 0;
+    for (int bb = b0; bb < b1; ++bb) local += batch_tiles(a.indptr, bb);
+    // inclusive scan of the per-thread counts (Hillis-Steele in LDS)
+    lds_int* sc = tp_lds + kFusedPlanMax + 1;
+    sc[t] = local;
+    __syncthreads();
+    for (int off = 1; off < nthr; off <<= 1) {
+      const int add = t >= off ? sc[t - off] : 0;
+      __syncthreads();
+      sc[t] += add;
+      __syncthreads();
+    }
+    int run = t > 0 ? sc[t - 1] : 0;
+    for (int bb = b0; bb < b1; ++bb) {
+      tp_lds[bb] = run;
+      run += batch_tiles(a.indptr, bb);
+    }
+    if (t == nthr - 1) tp_lds[B] = sc[nthr - 1];
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int bb = t; bb <= B; bb += nthr) a.tile_ptr[bb] = tp_lds[bb];
+  }
+  auto tile_ptr = [&](int i) -> int {
+    if constexpr (FUSE) return tp_lds[i];
+    else return a.tile_ptr[i];
+  };
+
   const int P = gridDim.x, w = slice_of(blockIdx.x, P);
-  const int T = a.tile_ptr[a.B];
+  const int T = tile_ptr(a.B);
   int g = split_start(w, T, P);
   const int gend = split_start(w + 1, T, P);
   if (g >= gend) return;
@@ -213,14 +255,14 @@ void mla_split_kernel(MlaArgs a) {
     int lo = 0, up = a.B;  // tile_ptr[lo] <= g < tile_ptr[up]
     while (up - lo > 1) {
       const int mid = (lo + up) >> 1;
-      if (a.tile_ptr[mid] <= g) lo = mid; else up = mid;
+      if (tile_ptr(mid) <= g) lo = mid; else up = mid;
     }
     b = lo;
   }
 
   while (true) {
-    const int tb = a.tile_ptr[b];
-    const int seg_end = min(gend, a.tile_ptr[b + 1]);
+    const int tb = tile_ptr(b);
+    const int seg_end = min(gend, tile_ptr(b + 1));
     const int t0 = g - tb, nt = seg_end - g;
     const int kv_lo = a.indptr[b];
     const int kv_hi = a.indptr[b + 1];
@@ -397,7 +439,7 @@ void mla_split_kernel(MlaArgs a) {
 
     g = seg_end;
     if (g >= gend) break;
-    do { ++b; } while (a.tile_ptr[b + 1] <= g);
+    do { ++b; } while (tile_ptr(b + 1) <= g);
   }
 }
 
@@ -408,10 +450,12 @@ size_t mla_workspace_bytes(int B, int H, int n_split) {
   return align256((size_t)(B + 1) * 4) + align256(slots * H * 4) + slots * H * kDl * 2;
 }
 
-template <int NW, int NSTAGE>
+template <int NW, int NSTAGE, bool FUSE>
 static hipError_t launch_split(const MlaArgs& a, int n_split, hipStream_t stream) {
-  constexpr size_t lds = (size_t)NSTAGE * kStage;
-  auto kern = mla_split_kernel<NW, NSTAGE>;
+  // ring, then (fused plan) the tile prefix and the scan scratch
+  constexpr size_t lds = (size_t)NSTAGE * kStage + (size_t)(kFusedPlanMax + 1 + NW * 64) * 4;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto kern = mla_split_kernel<NW, NSTAGE, FUSE>;
   static const hipError_t attr_err =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr_err != hipSuccess) return attr_err;
@@ -440,13 +484,17 @@ hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, co
   a.part_lse = (float*)(ws + ints);
   a.part_o = (uint16_t*)(ws + ints + align256(slots * H * 4));
 
-  hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
+  const bool fuse = B < kFusedPlanMax;
+  if (!fuse) {
+    hipLaunchKernelGGL(mla_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   switch (H) {
-    case 128: e = launch_split<4, 4>(a, n_split, stream); break;
-    case 64: e = launch_split<2, 4>(a, n_split, stream); break;
-    default: e = launch_split<1, 3>(a, n_split, stream); break;
+    case 128: e = fuse ? launch_split<4, 4, true>(a, n_split, stream) : launch_split<4, 4, false>(a, n_split, stream); break;
+    case 64: e = fuse ? launch_split<2, 4, true>(a, n_split, stream) : launch_split<2, 4, false>(a, n_split, stream); break;
+    default: e = fuse ? launch_split<1, 3, true>(a, n_split, stream) : launch_split<1, 3, false>(a, n_split, stream); break;
   }
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3(B, (H + 7) / 8), dim3(256), 0, stream, a, n_split);
