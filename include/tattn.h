@@ -144,10 +144,14 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
  * A batch with no keys gets O = 0 and LSE = -inf. Work is split along the
  * packed key axis over the GPU's compute units; each piece writes a
  * normalised partial output and its log-sum-exp into a device workspace
- * that is allocated and freed in stream order on `stream`
- * ((CUs + B) * H * (512 * 2 + 4) bytes plus the split plan), and a second kernel
- * merges the pieces of each batch. TATTN_ERR_OOM if that workspace cannot
- * be allocated.
+ * ((CUs + B) * H * (512 * 2 + 4) bytes plus the split plan), and a second
+ * kernel merges the pieces of each batch. The library keeps one such
+ * workspace per device for the life of the process: a call that needs more
+ * than it holds waits for the previous call's kernels, frees it and
+ * allocates a larger one with hipMalloc (TATTN_ERR_OOM if that fails); any
+ * other call allocates nothing. A call made on a different stream from the
+ * previous one first makes its stream wait for that call's kernels, so calls
+ * on several streams of one device are correct but run one after another.
  */
 int mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe,
                void* o, float* lse, int B, int H, const int32_t* kv_indptr,

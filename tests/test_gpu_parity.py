@@ -296,3 +296,53 @@ def test_mla_decode_workload_sampled(ta, dev):
 
 def test_mla_ragged_workload_sampled(ta, dev):
     _sampled_mla(ta, dev, "mla_decode_ragged_bf16", 48)
+
+
+def _mla_dev_inputs(dev, B, H, seed, kv_len_range):
+    m = inputs.mla_inputs(B, H, seed=seed, kv_len_range=kv_len_range)
+    args = [to_dev(m[n], dev) for n in ("q", "q_pe", "kv", "k_pe")] + [to_dev(m["indptr"], dev)]
+    return m, args
+
+
+def test_mla_workspace_grows_and_is_reused(ta, dev):
+    # the library's decode workspace grows to the largest call and is reused;
+    # calls enqueued back to back without a synchronisation in between must
+    # each see their own partials
+    scale = float(np.float32(576 ** -0.5))
+    small, sa = _mla_dev_inputs(dev, 2, 128, 31, (1, 900))
+    big, ba = _mla_dev_inputs(dev, 600, 32, 32, (1, 40))
+    o1, l1 = ta.mla_decode(*sa, scale)
+    o2, l2 = ta.mla_decode(*ba, scale)  # needs a larger workspace
+    o3, l3 = ta.mla_decode(*sa, scale)
+    o4, l4 = ta.mla_decode(*ba, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(l1, l3)
+    assert torch.equal(o2, o4) and torch.equal(l2, l4)
+    ro, rl = oracle.mla_decode(*_mla_vals(small), small["indptr"], scale)
+    assert_bf16_parity(to_np(o1), to_np(l1), ro, rl, "mla small after growth")
+    ro, rl = oracle.mla_decode(*_mla_vals(big), big["indptr"], scale)
+    assert_bf16_parity(to_np(o2), to_np(l2), ro, rl, "mla big")
+
+
+def test_mla_calls_on_two_streams(ta, dev):
+    # calls on two streams share the device's workspace one after another
+    scale = float(np.float32(576 ** -0.5))
+    ma, aa = _mla_dev_inputs(dev, 16, 128, 33, (1, 2000))
+    mb, ab = _mla_dev_inputs(dev, 9, 64, 34, (1, 3000))
+    ra = ta.mla_decode(*aa, scale)
+    rb = ta.mla_decode(*ab, scale)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    outs = []
+    for rep in range(3):
+        with torch.cuda.stream(s1):
+            xa = ta.mla_decode(*aa, scale)
+        with torch.cuda.stream(s2):
+            xb = ta.mla_decode(*ab, scale)
+        outs.append((xa, xb))
+    torch.cuda.synchronize()
+    for xa, xb in outs:
+        assert torch.equal(xa[0], ra[0]) and torch.equal(xa[1], ra[1])
+        assert torch.equal(xb[0], rb[0]) and torch.equal(xb[1], rb[1])
+    ro, rl = oracle.mla_decode(*_mla_vals(mb), mb["indptr"], scale)
+    assert_bf16_parity(to_np(rb[0]), to_np(rb[1]), ro, rl, "mla stream b")

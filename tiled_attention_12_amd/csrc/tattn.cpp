@@ -1,5 +1,5 @@
 // C ABI of libtattn.so: argument validation, dispatch to the gfx950
-// launchers, stream-ordered workspace for the split decode. See
+// launchers, the per-device workspace of the split decode. See
 // include/tattn.h for the contract of every entry point.
 #include "tattn.h"
 
@@ -50,6 +50,19 @@ int have_device() {
   int dev = -1;
   return (hipGetDevice(&dev) == hipSuccess && dev >= 0) ? TATTN_OK : TATTN_ERR_HIP;
 }
+
+// Decode workspace of one device: grown (never shrunk) to the largest size a
+// call has needed and kept until the process ends. `done` is recorded on the
+// stream of the last call that used it; the next call's stream waits for it,
+// so calls on different streams never share the buffer at the same time.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipEvent_t done = nullptr;
+};
+
+std::mutex g_ws_mu;
+Workspace g_ws[256];
 
 // Shared validation of the two MHA entry points. Returns TATTN_OK with
 // *nothing = true when there is no work.
@@ -130,17 +143,35 @@ TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const 
   if (const char* cap = std::getenv("TATTN_WS_LIMIT_BYTES")) {
     if (bytes > (size_t)std::strtoull(cap, nullptr, 10)) return TATTN_ERR_OOM;
   }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return TATTN_ERR_HIP;
   hipStream_t s = (hipStream_t)stream;
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, s);
-  if (e != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return TATTN_ERR_OOM;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[dev];
+  if (!w.done && hipEventCreateWithFlags(&w.done, hipEventDisableTiming) != hipSuccess) {
+    w.done = nullptr;
+    return TATTN_ERR_HIP;
   }
-  e = tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, cus, ws, s);
-  const hipError_t ef = hipFreeAsync(ws, s);
+  if (w.bytes < bytes) {
+    // the old buffer may still be in use by the last call's kernels
+    if (w.ptr) {
+      if (hipEventSynchronize(w.done) != hipSuccess || hipFree(w.ptr) != hipSuccess) return TATTN_ERR_HIP;
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    if (hipMalloc(&w.ptr, bytes) != hipSuccess || !w.ptr) {
+      (void)hipGetLastError();
+      w.ptr = nullptr;
+      return TATTN_ERR_OOM;
+    }
+    w.bytes = bytes;
+  } else if (hipStreamWaitEvent(s, w.done, 0) != hipSuccess) {
+    return TATTN_ERR_HIP;
+  }
+  const hipError_t e = tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, cus, w.ptr, s);
+  const hipError_t er = hipEventRecord(w.done, s);
   if (e != hipSuccess) return status_of(e);
-  return status_of(ef);
+  return status_of(er);
 }
 
 TATTN_API const char* tattn_status_str(int status) {
