@@ -33,9 +33,12 @@
 //    2^8 (in base-2 units), so the O rescale runs on few tiles; every
 //    exponential stays <= 2^8 and the result is unchanged (both O and l are
 //    taken relative to the same m).
-//  * Workgroup -> tile order: the hardware hands workgroup i to XCD i % 8;
-//    all query tiles of a (batch, head) are sent to one XCD so its K/V stays
-//    in that XCD's L2, and causal launches run the longest tiles first.
+//  * Persistent grid: one workgroup per compute unit loops over work items
+//    (one 256-row query tile of one (batch, head) each). The hardware hands
+//    workgroup i to XCD i % 8 and item i runs on XCD i % 8 too: all query
+//    tiles of a (batch, head) go to one XCD so its K/V stays in that XCD's
+//    L2. Causal items are taken longest first, and each workgroup's passes
+//    alternate direction so long and short tiles pair up.
 #include "device_common.h"
 #include "launch.h"
 
@@ -67,6 +70,7 @@ struct MhaArgs {
   int window; // key window half-width (0: none)
   const uint8_t* bmask;  // [B, H, nqb, nkb] per 64x64 block, or null
   int nqb, nkb;
+  int n_items;  // n_qtiles * n_bh
 };
 
 // Block size of the block mask: 64 query rows x 64 keys (one key tile; each
@@ -101,389 +105,416 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int hi = lane >> 5;      // wave half
   const int col = lane & 31;     // query column owned by the lane
 
-  int bh, qt;
-  {
-    const int i = blockIdx.x;
-    int rank;
-    if (a.remap) {
-      const int nbh_x = a.n_bh >> 3, local = i >> 3, xcd = i & 7;
-      rank = local / nbh_x;
-      bh = xcd * nbh_x + (local - rank * nbh_x);
-    } else {
-      rank = i / a.n_bh;
-      bh = i - rank * a.n_bh;
+  // One work item = one (batch*head, 256-row query tile). The grid is
+  // persistent (at most one workgroup per compute unit); item i runs where
+  // workgroup i would: on XCD i % 8.
+  auto process = [&](const int i) {
+    int bh, qt;
+    {
+      int rank;
+      if (a.remap) {
+        const int nbh_x = a.n_bh >> 3, local = i >> 3, xcd = i & 7;
+        rank = local / nbh_x;
+        bh = xcd * nbh_x + (local - rank * nbh_x);
+      } else {
+        rank = i / a.n_bh;
+        bh = i - rank * a.n_bh;
+      }
+      qt = CAUSAL ? a.n_qtiles - 1 - rank : rank;
     }
-    qt = CAUSAL ? a.n_qtiles - 1 - rank : rank;
-  }
 
-  const int Sq = a.Sq, Skv = a.Skv;
-  const int q0 = qt * BR;
-  const int wrow0 = q0 + wave * 32;
-  const uint16_t* qp = a.q + (size_t)bh * Sq * D;
-  // query head h of batch b reads KV head h / group
-  const int bq = bh / a.H, hq = bh - bq * a.H;
-  const size_t kvh = (size_t)bq * (a.H / a.group) + hq / a.group;
-  const char* kp = (const char*)(a.k + kvh * Skv * D);
-  const char* vp = (const char*)(a.v + kvh * Skv * D);
-  const float c = a.c;
+    const int Sq = a.Sq, Skv = a.Skv;
+    const int q0 = qt * BR;
+    const int wrow0 = q0 + wave * 32;
+    const uint16_t* qp = a.q + (size_t)bh * Sq * D;
+    // query head h of batch b reads KV head h / group
+    const int bq = bh / a.H, hq = bh - bq * a.H;
+    const size_t kvh = (size_t)bq * (a.H / a.group) + hq / a.group;
+    const char* kp = (const char*)(a.k + kvh * Skv * D);
+    const char* vp = (const char*)(a.v + kvh * Skv * D);
+    const float c = a.c;
 
-  int kv_end = Skv;
-  if (CAUSAL) {
-    const int last = min(q0 + BR, Sq) - 1;
-    kv_end = max(0, min(Skv, last + Skv - Sq + 1));
-  }
-  const int nt = (kv_end + BC - 1) / BC;
-  // last key this wave's rows can see (causal); tiles past it are skipped
-  const int wave_kv_last = CAUSAL ? min(wrow0 + 31, Sq - 1) + Skv - Sq : Skv - 1;
-
-  // Lane-dependent LDS address parts. The XOR swizzle touches only the low
-  // 4 chunk bits and depends only on the low 4 row bits, so the key block,
-  // row half, K/V choice and stage are immediate offsets.
-  const uint32_t smem0 = lds_addr(smem);
-  uint32_t kbase[KS];
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kbase[ks] = smem0 + col * RS + 16 * swz<CPR>(col, 2 * ks + hi);
-  uint32_t vbase[2][DB];
-  {
-    const int gq = (lane >> 4) & 1, s16 = lane & 15;
-    const int x = 2 * gq + ((s16 & 3) >> 1), boff = 8 * (s16 & 1);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int rr = 8 * e + 4 * hi + (s16 >> 2);
-#pragma unroll
-      for (int db = 0; db < DB; ++db) vbase[e][db] = smem0 + VREG + rr * RS + 16 * swz<CPR>(rr, db * 4 + x) + boff;
+    int kv_end = Skv;
+    if (CAUSAL) {
+      const int last = min(q0 + BR, Sq) - 1;
+      kv_end = max(0, min(Skv, last + Skv - Sq + 1));
     }
-  }
+    const int nt = (kv_end + BC - 1) / BC;
+    // last key this wave's rows can see (causal); tiles past it are skipped
+    const int wave_kv_last = CAUSAL ? min(wrow0 + 31, Sq - 1) + Skv - Sq : Skv - 1;
 
-  // Tile t -> stage ST: wave loads n cover chunk slots (n*NW + wave)*64 + lane.
-  auto issue = [&](int t, auto STc) {
-    constexpr int ST = decltype(STc)::value;
-    const int lim = Skv - 1 - t * BC;  // >= 0: tile t has a visible key
-    const char* kt = kp + (size_t)t * BC * RS;
-    const char* vt = vp + (size_t)t * BC * RS;
-#pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-      const int slot = (n * NW + wave) * 64 + lane;
-      const int row = slot / CPR;
-      const uint32_t off = (uint32_t)(min(row, lim) * RS + 16 * swz<CPR>(row, slot % CPR));
-      const uint32_t dst = smem0 + ST * TILE + (n * NW + wave) * 1024;
-      load_lds16_asm(kt + off, dst);
-      load_lds16_asm(vt + off, dst + VREG);
-    }
-  };
-
-  if constexpr (!EXT) {
-    static_for<PF>([&](auto Ic) {
-      if (decltype(Ic)::value < nt) issue(decltype(Ic)::value, Ic);
-    });
-  }
-  // wait until this wave's loads of tile t have landed (tiles up to
-  // t + PF - 1 may still be in flight)
-  auto wait_tile = [&](int t) {
-    if constexpr (PF == 2) {
-      if (t + 1 < nt) {
-        wait_vmcnt<LPT>();
-        return;
+    // Lane-dependent LDS address parts. The XOR swizzle touches only the low
+    // 4 chunk bits and depends only on the low 4 row bits, so the key block,
+    // row half, K/V choice and stage are immediate offsets.
+    const uint32_t smem0 = lds_addr(smem);
+    uint32_t kbase[KS];
+  #pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kbase[ks] = smem0 + col * RS + 16 * swz<CPR>(col, 2 * ks + hi);
+    uint32_t vbase[2][DB];
+    {
+      const int gq = (lane >> 4) & 1, s16 = lane & 15;
+      const int x = 2 * gq + ((s16 & 3) >> 1), boff = 8 * (s16 & 1);
+  #pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int rr = 8 * e + 4 * hi + (s16 >> 2);
+  #pragma unroll
+        for (int db = 0; db < DB; ++db) vbase[e][db] = smem0 + VREG + rr * RS + 16 * swz<CPR>(rr, db * 4 + x) + boff;
       }
     }
-    wait_vmcnt<0>();
-  };
 
-  // Q^T fragments (B operand), loaded once.
-  bf16x8 qf[KS];
-  {
-    const int row = wrow0 + col;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      u32x4 x = {0, 0, 0, 0};
-      if (row < Sq) x = *(const u32x4*)(qp + (size_t)row * D + ks * 16 + hi * 8);
-      qf[ks] = as_bf16x8(x);
+    // Tile t -> stage ST: wave loads n cover chunk slots (n*NW + wave)*64 + lane.
+    auto issue = [&](int t, auto STc) {
+      constexpr int ST = decltype(STc)::value;
+      const int lim = Skv - 1 - t * BC;  // >= 0: tile t has a visible key
+      const char* kt = kp + (size_t)t * BC * RS;
+      const char* vt = vp + (size_t)t * BC * RS;
+  #pragma unroll
+      for (int n = 0; n < LOADS; ++n) {
+        const int slot = (n * NW + wave) * 64 + lane;
+        const int row = slot / CPR;
+        const uint32_t off = (uint32_t)(min(row, lim) * RS + 16 * swz<CPR>(row, slot % CPR));
+        const uint32_t dst = smem0 + ST * TILE + (n * NW + wave) * 1024;
+        load_lds16_asm(kt + off, dst);
+        load_lds16_asm(vt + off, dst + VREG);
+      }
+    };
+
+    if constexpr (!EXT) {
+      static_for<PF>([&](auto Ic) {
+        if (decltype(Ic)::value < nt) issue(decltype(Ic)::value, Ic);
+      });
     }
-  }
+    // wait until this wave's loads of tile t have landed (tiles up to
+    // t + PF - 1 may still be in flight)
+    auto wait_tile = [&](int t) {
+      if constexpr (PF == 2) {
+        if (t + 1 < nt) {
+          wait_vmcnt<LPT>();
+          return;
+        }
+      }
+      wait_vmcnt<0>();
+    };
 
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
-  float m = -INFINITY, lsum = 0.f;
+    // Q^T fragments (B operand), loaded once.
+    bf16x8 qf[KS];
+    {
+      const int row = wrow0 + col;
+  #pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        u32x4 x = {0, 0, 0, 0};
+        if (row < Sq) x = *(const u32x4*)(qp + (size_t)row * D + ks * 16 + hi * 8);
+        qf[ks] = as_bf16x8(x);
+      }
+    }
 
-  // ---- the three phases of one tile (stage ST):
-  //   M1: S^T = K*Q^T (MFMA), V: masks + online softmax (VALU), M2: O^T += V^T*P^T (MFMA)
-  auto m1 = [&](auto STc, f32x16 (&s)[KB]) {
-    constexpr int ST = decltype(STc)::value;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
-    // k-steps in groups of 2; inside a group the key blocks alternate, so
-    // consecutive MFMAs never depend on each other. The K fragments of group
-    // g+1 are read while group g's MFMAs run.
-    auto rd = [&](auto Gc, bf16x8 (&kf)[2][KB]) {
-      constexpr int g = decltype(Gc)::value;
-      static_for<2>([&](auto Uc) {
-        static_for<KB>([&](auto KBc) {
-          kf[Uc][KBc] = as_bf16x8(lds_read128(
-              (const void*)(uintptr_t)(kbase[2 * g + Uc] + ST * TILE + decltype(KBc)::value * 32 * RS)));
+    f32x16 oacc[DB];
+  #pragma unroll
+    for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
+    float m = -INFINITY, lsum = 0.f;
+
+    // ---- the three phases of one tile (stage ST):
+    //   M1: S^T = K*Q^T (MFMA), V: masks + online softmax (VALU), M2: O^T += V^T*P^T (MFMA)
+    auto m1 = [&](auto STc, f32x16 (&s)[KB]) {
+      constexpr int ST = decltype(STc)::value;
+  #pragma unroll
+      for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
+      // k-steps in groups of 2; inside a group the key blocks alternate, so
+      // consecutive MFMAs never depend on each other. The K fragments of group
+      // g+1 are read while group g's MFMAs run.
+      auto rd = [&](auto Gc, bf16x8 (&kf)[2][KB]) {
+        constexpr int g = decltype(Gc)::value;
+        static_for<2>([&](auto Uc) {
+          static_for<KB>([&](auto KBc) {
+            kf[Uc][KBc] = as_bf16x8(lds_read128(
+                (const void*)(uintptr_t)(kbase[2 * g + Uc] + ST * TILE + decltype(KBc)::value * 32 * RS)));
+          });
+        });
+      };
+      bf16x8 kf[2][2][KB];
+      rd(std::integral_constant<int, 0>{}, kf[0]);
+      static_for<KS / 2>([&](auto Gc) {
+        constexpr int g = decltype(Gc)::value;
+        if constexpr (g + 1 < KS / 2) rd(std::integral_constant<int, g + 1>{}, kf[(g + 1) % 2]);
+        static_for<2>([&](auto Uc) {
+          static_for<KB>([&](auto KBc) { s[KBc] = mfma32(kf[g % 2][Uc][KBc], qf[2 * g + Uc], s[KBc]); });
         });
       });
     };
-    bf16x8 kf[2][2][KB];
-    rd(std::integral_constant<int, 0>{}, kf[0]);
-    static_for<KS / 2>([&](auto Gc) {
-      constexpr int g = decltype(Gc)::value;
-      if constexpr (g + 1 < KS / 2) rd(std::integral_constant<int, g + 1>{}, kf[(g + 1) % 2]);
-      static_for<2>([&](auto Uc) {
-        static_for<KB>([&](auto KBc) { s[KBc] = mfma32(kf[g % 2][Uc][KBc], qf[2 * g + Uc], s[KBc]); });
-      });
-    });
-  };
 
-  // V, first part: masks, tile max, and (rarely) raising the running max
-  auto vmax = [&](int t, f32x16 (&s)[KB], auto MASKEDc) {
-    const int kv0 = t * BC;
-    if constexpr (decltype(MASKEDc)::value) {
-      // key j is visible to this lane's row when lo <= j <= lim
-      const int pos = wrow0 + col + Skv - Sq;
-      int lim = CAUSAL ? min(Skv - 1, pos) : Skv - 1;
-      int lo = 0;
-      if constexpr (EXT) {
-        if (a.window > 0) {
-          lim = min(lim, pos + a.window - 1);
-          lo = pos - a.window;
+    // V, first part: masks, tile max, and (rarely) raising the running max
+    auto vmax = [&](int t, f32x16 (&s)[KB], auto MASKEDc) {
+      const int kv0 = t * BC;
+      if constexpr (decltype(MASKEDc)::value) {
+        // key j is visible to this lane's row when lo <= j <= lim
+        const int pos = wrow0 + col + Skv - Sq;
+        int lim = CAUSAL ? min(Skv - 1, pos) : Skv - 1;
+        int lo = 0;
+        if constexpr (EXT) {
+          if (a.window > 0) {
+            lim = min(lim, pos + a.window - 1);
+            lo = pos - a.window;
+          }
         }
+  #pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = kv0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
+            if (j > lim || j < lo) s[kb][i] = -INFINITY;
+          }
       }
-#pragma unroll
+      float mx = -INFINITY;
+  #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = kv0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-          if (j > lim || j < lo) s[kb][i] = -INFINITY;
-        }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = max_halves(mx) * c;
-    const bool raise = mx - m > TAU;  // false when mx == -inf
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float alpha = raise ? fast_exp2(m - mx) : 1.f;
-      m = raise ? mx : m;
-      lsum *= alpha;
-#pragma unroll
-      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-    }
-  };
-  // V, second part: exponentials, row sums, P^T in bf16
-  auto vexp = [&](const f32x16 (&s)[KB], bf16x8 (&pf)[KB][2]) {
-    const float mc = m == -INFINITY ? 0.f : m;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        float p[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          p[j] = fast_exp2(fmaf(s[kb][half * 8 + j], c, -mc));
-          lsum += p[j];
-        }
-        u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                   pack_bf16x2(p[6], p[7])};
-        pf[kb][half] = as_bf16x8(w);
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = max_halves(mx) * c;
+      const bool raise = mx - m > TAU;  // false when mx == -inf
+      if (__builtin_amdgcn_ballot_w64(raise)) {
+        const float alpha = raise ? fast_exp2(m - mx) : 1.f;
+        m = raise ? mx : m;
+        lsum *= alpha;
+  #pragma unroll
+        for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       }
-  };
-  auto vphase = [&](int t, f32x16 (&s)[KB], bf16x8 (&pf)[KB][2], auto MASKEDc) {
-    vmax(t, s, MASKEDc);
-    vexp(s, pf);
-  };
-
-  auto m2 = [&](auto STc, const bf16x8 (&pf)[KB][2]) {
-    constexpr int ST = decltype(STc)::value;
-    // for each 16-key slice: read the V^T fragments of all d-blocks, then one
-    // MFMA per d-block (independent accumulators back to back)
-    static_for<KB * 2>([&](auto SC) {
-      constexpr int kb = decltype(SC)::value / 2, half = decltype(SC)::value % 2;
-      constexpr int off = ST * TILE + kb * 32 * RS + half * 16 * RS;
-      bf16x8 vf[DB];
-      static_for<DB>([&](auto DBc) {
-        const u32x2 r0 = lds_read_tr16<off>(vbase[0][DBc]);
-        const u32x2 r1 = lds_read_tr16<off>(vbase[1][DBc]);
-        vf[DBc] = cat_tr(r0, r1);
-      });
-      static_for<DB>([&](auto DBc) { oacc[DBc] = mfma32(vf[DBc], pf[kb][half], oacc[DBc]); });
-    });
-  };
-
-  if constexpr (EXT) {
-    // Sliding window and/or block mask: the workgroup walks only the key
-    // tiles that some of its rows can see and that the block mask keeps,
-    // one tile in flight; a wave whose own rows see nothing of a tile (or
-    // whose query block masks it) skips that tile's arithmetic. Every such
-    // tile is masked per element (window edges, causal diagonal, tail).
-    const int W = a.window;
-    const int off = Skv - Sq;
-    const int last_row = min(q0 + BR, Sq) - 1;
-    int lo = 0, hi = Skv;
-    if (CAUSAL) hi = min(hi, last_row + off + 1);
-    if (W > 0) {
-      lo = max(0, q0 + off - W);
-      hi = min(hi, last_row + off + W);
-    }
-    const int t_first = lo / BC;
-    const int t_end = hi > lo ? (hi + BC - 1) / BC : t_first;
-    const int wlast = min(wrow0 + 31, Sq - 1);
-    int wlo = 0, whi = Skv;
-    if (CAUSAL) whi = min(whi, wlast + off + 1);
-    if (W > 0) {
-      wlo = max(0, wrow0 + off - W);
-      whi = min(whi, wlast + off + W);
-    }
-    const bool wave_rows = wrow0 < Sq;
-    const uint8_t* mrow = a.bmask ? a.bmask + (size_t)bh * a.nqb * a.nkb : nullptr;
-    const int qb_first = q0 / kMaskBlock, qb_last = last_row / kMaskBlock, qb_w = wrow0 / kMaskBlock;
-    auto active = [&](int t) {
-      if (!mrow) return true;
-      int any = 0;
-      for (int qb = qb_first; qb <= qb_last; ++qb) any |= mrow[qb * a.nkb + t];
-      return any != 0;
     };
-    auto next_active = [&](int t) {
-      do { ++t; } while (t < t_end && !active(t));
-      return t;
-    };
-    f32x16 sx[KB];
-    int cur = t_first;
-    if (cur < t_end && !active(cur)) cur = next_active(cur);
-    if (cur < t_end) issue(cur, std::integral_constant<int, 0>{});
-    for (int cnt = 0; cur < t_end; ++cnt) {
-      // mask bytes are read before the next refill is issued, so waiting for
-      // them never waits for that refill
-      const int nxt = next_active(cur);
-      const bool wact = wave_rows && cur * BC < whi && (cur + 1) * BC > wlo &&
-                        (!mrow || mrow[qb_w * a.nkb + cur] != 0);
-      const int st = cnt % NSTAGE;
-      static_for<NSTAGE>([&](auto STc) {
-        constexpr int ST = decltype(STc)::value;
-        if (st != ST) return;
-        wait_vmcnt<0>();
-        wait_lgkmcnt0();
-        barrier();
-        if (nxt < t_end) issue(nxt, std::integral_constant<int, (ST + 1) % NSTAGE>{});
-        if (wact) {
-          bf16x8 pf[KB][2];
-          m1(STc, sx);
-          vphase(cur, sx, pf, std::true_type{});
-          m2(STc, pf);
+    // V, second part: exponentials, row sums, P^T in bf16
+    auto vexp = [&](const f32x16 (&s)[KB], bf16x8 (&pf)[KB][2]) {
+      const float mc = m == -INFINITY ? 0.f : m;
+  #pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+  #pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          float p[8];
+  #pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            p[j] = fast_exp2(fmaf(s[kb][half * 8 + j], c, -mc));
+            lsum += p[j];
+          }
+          u32x4 w = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                     pack_bf16x2(p[6], p[7])};
+          pf[kb][half] = as_bf16x8(w);
         }
+    };
+    auto vphase = [&](int t, f32x16 (&s)[KB], bf16x8 (&pf)[KB][2], auto MASKEDc) {
+      vmax(t, s, MASKEDc);
+      vexp(s, pf);
+    };
+
+    auto m2 = [&](auto STc, const bf16x8 (&pf)[KB][2]) {
+      constexpr int ST = decltype(STc)::value;
+      // for each 16-key slice: read the V^T fragments of all d-blocks, then one
+      // MFMA per d-block (independent accumulators back to back)
+      static_for<KB * 2>([&](auto SC) {
+        constexpr int kb = decltype(SC)::value / 2, half = decltype(SC)::value % 2;
+        constexpr int off = ST * TILE + kb * 32 * RS + half * 16 * RS;
+        bf16x8 vf[DB];
+        static_for<DB>([&](auto DBc) {
+          const u32x2 r0 = lds_read_tr16<off>(vbase[0][DBc]);
+          const u32x2 r1 = lds_read_tr16<off>(vbase[1][DBc]);
+          vf[DBc] = cat_tr(r0, r1);
+        });
+        static_for<DB>([&](auto DBc) { oacc[DBc] = mfma32(vf[DBc], pf[kb][half], oacc[DBc]); });
       });
-      cur = nxt;
-    }
-  } else {
-    // Every wave runs one tile behind itself: after barrier t it forms the
-    // scores of tile t (MFMA) while it exponentiates those of tile t-1 (VALU),
-    // then accumulates P*V of tile t-1, and the refill of tile t+PF is in
-    // flight. The scores alternate between two register sets; the loop is
-    // unrolled over UN tiles (a multiple of both the stage count and 2) so
-    // every stage offset and register set is a compile-time constant. The
-    // refill issued at barrier t targets stage (t+PF) % NSTAGE, last read by
-    // P*V of tile t-2 before that barrier.
-    f32x16 sb[2][KB];
-    f32x16 (&s_cur)[KB] = sb[0];
-    int t_plain = Skv / BC;
-    if (CAUSAL) t_plain = min(t_plain, max(0, (q0 + Skv - Sq + 1) / BC));
-    t_plain = min(t_plain, nt);
-    // pipelined tiles: 0 .. t_main-1 with t_main = 1 + UN*k
-    const int t_main = t_plain >= 1 ? 1 + UN * ((t_plain - 1) / UN) : 0;
-    if (t_main > 0) {
-      wait_tile(0);
-      wait_lgkmcnt0();
-      barrier();
-      if (PF < nt) issue(PF, std::integral_constant<int, PF % NSTAGE>{});
-      m1(std::integral_constant<int, 0>{}, sb[0]);
-      for (int t0 = 0; t0 + 1 < t_main; t0 += UN) {
-        static_for<UN>([&](auto Uc) {
-          constexpr int U = decltype(Uc)::value + 1;          // tile t0 + U
-          constexpr int ST = U % NSTAGE, SP = (U - 1) % NSTAGE;
-          constexpr int BN = U % 2, BP = (U - 1) % 2;
-          const int t = t0 + U;
-          wait_tile(t);
+    };
+
+    if constexpr (EXT) {
+      // Sliding window and/or block mask: the workgroup walks only the key
+      // tiles that some of its rows can see and that the block mask keeps,
+      // one tile in flight; a wave whose own rows see nothing of a tile (or
+      // whose query block masks it) skips that tile's arithmetic. Every such
+      // tile is masked per element (window edges, causal diagonal, tail).
+      const int W = a.window;
+      const int off = Skv - Sq;
+      const int last_row = min(q0 + BR, Sq) - 1;
+      int lo = 0, hi = Skv;
+      if (CAUSAL) hi = min(hi, last_row + off + 1);
+      if (W > 0) {
+        lo = max(0, q0 + off - W);
+        hi = min(hi, last_row + off + W);
+      }
+      const int t_first = lo / BC;
+      const int t_end = hi > lo ? (hi + BC - 1) / BC : t_first;
+      const int wlast = min(wrow0 + 31, Sq - 1);
+      int wlo = 0, whi = Skv;
+      if (CAUSAL) whi = min(whi, wlast + off + 1);
+      if (W > 0) {
+        wlo = max(0, wrow0 + off - W);
+        whi = min(whi, wlast + off + W);
+      }
+      const bool wave_rows = wrow0 < Sq;
+      const uint8_t* mrow = a.bmask ? a.bmask + (size_t)bh * a.nqb * a.nkb : nullptr;
+      const int qb_first = q0 / kMaskBlock, qb_last = last_row / kMaskBlock, qb_w = wrow0 / kMaskBlock;
+      auto active = [&](int t) {
+        if (!mrow) return true;
+        int any = 0;
+        for (int qb = qb_first; qb <= qb_last; ++qb) any |= mrow[qb * a.nkb + t];
+        return any != 0;
+      };
+      auto next_active = [&](int t) {
+        do { ++t; } while (t < t_end && !active(t));
+        return t;
+      };
+      f32x16 sx[KB];
+      int cur = t_first;
+      if (cur < t_end && !active(cur)) cur = next_active(cur);
+      if (cur < t_end) issue(cur, std::integral_constant<int, 0>{});
+      for (int cnt = 0; cur < t_end; ++cnt) {
+        // mask bytes are read before the next refill is issued, so waiting for
+        // them never waits for that refill
+        const int nxt = next_active(cur);
+        const bool wact = wave_rows && cur * BC < whi && (cur + 1) * BC > wlo &&
+                          (!mrow || mrow[qb_w * a.nkb + cur] != 0);
+        const int st = cnt % NSTAGE;
+        static_for<NSTAGE>([&](auto STc) {
+          constexpr int ST = decltype(STc)::value;
+          if (st != ST) return;
+          wait_vmcnt<0>();
           wait_lgkmcnt0();
           barrier();
-          if (t + PF < nt) issue(t + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
-          vmax(t - 1, sb[BP], std::false_type{});
-          bf16x8 pf[KB][2];
-          vexp(sb[BP], pf);
-          m1(std::integral_constant<int, ST>{}, sb[BN]);
-          m2(std::integral_constant<int, SP>{}, pf);
-          // MFMAs of the scores alternate with the exponentials' VALU work,
-          // each group of K-fragment reads one step ahead; then P*V.
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2 * KB, 0);
-          static_for<KS * KB>([&](auto Ic) {
-            constexpr int i = decltype(Ic)::value;
-            constexpr int ahead = 2 * 2 * KB;  // reads issued before MFMA i
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, TATTN_VALU_PER_MFMA, 0);
-            if constexpr (i % (2 * KB) == 2 * KB - 1 && i + 1 + ahead <= KS * KB)
-              __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
+          if (nxt < t_end) issue(nxt, std::integral_constant<int, (ST + 1) % NSTAGE>{});
+          if (wact) {
+            bf16x8 pf[KB][2];
+            m1(STc, sx);
+            vphase(cur, sx, pf, std::true_type{});
+            m2(STc, pf);
+          }
+        });
+        cur = nxt;
+      }
+    } else {
+      // Every wave runs one tile behind itself: after barrier t it forms the
+      // scores of tile t (MFMA) while it exponentiates those of tile t-1 (VALU),
+      // then accumulates P*V of tile t-1, and the refill of tile t+PF is in
+      // flight. The scores alternate between two register sets; the loop is
+      // unrolled over UN tiles (a multiple of both the stage count and 2) so
+      // every stage offset and register set is a compile-time constant. The
+      // refill issued at barrier t targets stage (t+PF) % NSTAGE, last read by
+      // P*V of tile t-2 before that barrier.
+      f32x16 sb[2][KB];
+      f32x16 (&s_cur)[KB] = sb[0];
+      int t_plain = Skv / BC;
+      if (CAUSAL) t_plain = min(t_plain, max(0, (q0 + Skv - Sq + 1) / BC));
+      t_plain = min(t_plain, nt);
+      // pipelined tiles: 0 .. t_main-1 with t_main = 1 + UN*k
+      const int t_main = t_plain >= 1 ? 1 + UN * ((t_plain - 1) / UN) : 0;
+      if (t_main > 0) {
+        wait_tile(0);
+        wait_lgkmcnt0();
+        barrier();
+        if (PF < nt) issue(PF, std::integral_constant<int, PF % NSTAGE>{});
+        m1(std::integral_constant<int, 0>{}, sb[0]);
+        for (int t0 = 0; t0 + 1 < t_main; t0 += UN) {
+          static_for<UN>([&](auto Uc) {
+            constexpr int U = decltype(Uc)::value + 1;          // tile t0 + U
+            constexpr int ST = U % NSTAGE, SP = (U - 1) % NSTAGE;
+            constexpr int BN = U % 2, BP = (U - 1) % 2;
+            const int t = t0 + U;
+            wait_tile(t);
+            wait_lgkmcnt0();
+            barrier();
+            if (t + PF < nt) issue(t + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
+            vmax(t - 1, sb[BP], std::false_type{});
+            bf16x8 pf[KB][2];
+            vexp(sb[BP], pf);
+            m1(std::integral_constant<int, ST>{}, sb[BN]);
+            m2(std::integral_constant<int, SP>{}, pf);
+            // MFMAs of the scores alternate with the exponentials' VALU work,
+            // each group of K-fragment reads one step ahead; then P*V.
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * 2 * KB, 0);
+            static_for<KS * KB>([&](auto Ic) {
+              constexpr int i = decltype(Ic)::value;
+              constexpr int ahead = 2 * 2 * KB;  // reads issued before MFMA i
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, TATTN_VALU_PER_MFMA, 0);
+              if constexpr (i % (2 * KB) == 2 * KB - 1 && i + 1 + ahead <= KS * KB)
+                __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 0);
+            });
+            static_for<KB * 2>([&](auto) {
+              __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
+              __builtin_amdgcn_sched_group_barrier(0x008, DB, 0);
+            });
           });
-          static_for<KB * 2>([&](auto) {
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, DB, 0);
-          });
+        }
+        // tile t_main - 1 (= UN*k: stage 0, set 0) still needs its softmax and P*V
+        bf16x8 pf[KB][2];
+        vphase(t_main - 1, sb[0], pf, std::false_type{});
+        m2(std::integral_constant<int, 0>{}, pf);
+      }
+
+      // the remaining tiles (causal diagonal, ragged tail) run masked, in order
+      auto tile_step = [&](int tt, auto STc) {
+        constexpr int ST = decltype(STc)::value;
+        wait_tile(tt);
+        wait_lgkmcnt0();
+        barrier();
+        if (tt + PF < nt) issue(tt + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
+        if (CAUSAL && tt * BC > wave_kv_last) return;
+        bf16x8 pf[KB][2];
+        m1(STc, s_cur);
+        vphase(tt, s_cur, pf, std::true_type{});
+        m2(STc, pf);
+      };
+      for (int t = t_main; t < nt; ++t) {
+        const int st = t % NSTAGE;
+        static_for<NSTAGE>([&](auto STc) {
+          if (st == decltype(STc)::value) tile_step(t, STc);
         });
       }
-      // tile t_main - 1 (= UN*k: stage 0, set 0) still needs its softmax and P*V
-      bf16x8 pf[KB][2];
-      vphase(t_main - 1, sb[0], pf, std::false_type{});
-      m2(std::integral_constant<int, 0>{}, pf);
+
     }
 
-    // the remaining tiles (causal diagonal, ragged tail) run masked, in order
-    auto tile_step = [&](int tt, auto STc) {
-      constexpr int ST = decltype(STc)::value;
-      wait_tile(tt);
-      wait_lgkmcnt0();
-      barrier();
-      if (tt + PF < nt) issue(tt + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
-      if (CAUSAL && tt * BC > wave_kv_last) return;
-      bf16x8 pf[KB][2];
-      m1(STc, s_cur);
-      vphase(tt, s_cur, pf, std::true_type{});
-      m2(STc, pf);
-    };
-    for (int t = t_main; t < nt; ++t) {
-      const int st = t % NSTAGE;
-      static_for<NSTAGE>([&](auto STc) {
-        if (st == decltype(STc)::value) tile_step(t, STc);
-      });
+    // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
+    {
+      const float l = sum_halves(lsum);
+      const int row = wrow0 + col;
+      if (row < Sq) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        uint16_t* orow = a.o + ((size_t)bh * Sq + row) * D;
+  #pragma unroll
+        for (int db = 0; db < DB; ++db)
+  #pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int d = db * 32 + 8 * g4 + 4 * hi;
+            u32x2 w = {pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv),
+                       pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
+            *(u32x2*)(orow + d) = w;
+          }
+        if (hi == 0) a.lse[(size_t)bh * Sq + row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+      }
     }
+  };
 
-  }
-
-  // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
-  {
-    const float l = sum_halves(lsum);
-    const int row = wrow0 + col;
-    if (row < Sq) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
-      uint16_t* orow = a.o + ((size_t)bh * Sq + row) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int d = db * 32 + 8 * g4 + 4 * hi;
-          u32x2 w = {pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv),
-                     pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
-          *(u32x2*)(orow + d) = w;
-        }
-      if (hi == 0) a.lse[(size_t)bh * Sq + row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+  // Items of XCD x are x + 8*local (local < L); workgroup w (XCD w % 8, the
+  // j-th of J there) takes local j, 2J-1-j, 2J+j, ... so that consecutive
+  // passes pair long causal tiles with short ones. Without the XCD order,
+  // workgroup w takes items w, w + G, ...
+  const int G = gridDim.x;
+  const int xq = blockIdx.x & 7, jq = blockIdx.x >> 3, J = G >> 3, L = a.n_items >> 3;
+  for (int k = 0;; ++k) {
+    int item = -1;
+    if (a.remap) {
+      if (k * J >= L) break;
+      const int local = (k & 1) ? (k + 1) * J - 1 - jq : k * J + jq;
+      if (local < L) item = xq + 8 * local;
+    } else {
+      item = blockIdx.x + k * G;
+      if (item >= a.n_items) break;
     }
+    if (item >= 0) process(item);
+    // every wave is done with the LDS ring before the next item refills it
+    wait_lgkmcnt0();
+    barrier();
   }
 }
 
 template <int D, int NW, int BC, bool CAUSAL, bool EXT>
-static hipError_t launch_one(const MhaArgs& a, hipStream_t stream) {
+static hipError_t launch_one(const MhaArgs& a, int n_cu, hipStream_t stream) {
   constexpr int BR = NW * 32;
   constexpr int NSTAGE = TATTN_MHA_STAGES;
   constexpr size_t lds = 2 * (size_t)NSTAGE * BC * D * 2;
+  static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = mha_fwd_bf16_kernel<D, NW, BC, NSTAGE, CAUSAL, EXT>;
   // Thread-safe one-time opt-in to more than the default dynamic LDS.
   static const hipError_t attr_err =
@@ -491,16 +522,21 @@ static hipError_t launch_one(const MhaArgs& a, hipStream_t stream) {
   if (attr_err != hipSuccess) return attr_err;
   MhaArgs b = a;
   b.n_qtiles = (a.Sq + BR - 1) / BR;
-  const long long grid = (long long)b.n_qtiles * a.n_bh;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  b.remap = (a.n_bh % 8) == 0;
+  const long long items = (long long)b.n_qtiles * a.n_bh;
+  if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  b.n_items = (int)items;
+  b.remap = (a.n_bh % 8) == 0 && n_cu >= 8;
+  // one workgroup per compute unit (LDS and registers allow no second one);
+  // a multiple of 8 for the XCD order
+  long long grid = items < n_cu ? items : n_cu;
+  if (b.remap) grid = (grid / 8) * 8;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, b);
   return hipGetLastError();
 }
 
 hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int Hkv, int Sq, int Skv, int D, bool causal, int window,
-                               const uint8_t* block_mask, float scale, hipStream_t stream) {
+                               const uint8_t* block_mask, float scale, int n_cu, hipStream_t stream) {
   MhaArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -519,11 +555,11 @@ hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void
   a.nkb = (Skv + kMaskBlock - 1) / kMaskBlock;
   const bool ext = window > 0 || block_mask != nullptr;
   if (ext) {
-    if (D == 128) return causal ? launch_one<128, 8, 64, true, true>(a, stream) : launch_one<128, 8, 64, false, true>(a, stream);
-    return causal ? launch_one<64, 8, 64, true, true>(a, stream) : launch_one<64, 8, 64, false, true>(a, stream);
+    if (D == 128) return causal ? launch_one<128, 8, 64, true, true>(a, n_cu, stream) : launch_one<128, 8, 64, false, true>(a, n_cu, stream);
+    return causal ? launch_one<64, 8, 64, true, true>(a, n_cu, stream) : launch_one<64, 8, 64, false, true>(a, n_cu, stream);
   }
-  if (D == 128) return causal ? launch_one<128, 8, 64, true, false>(a, stream) : launch_one<128, 8, 64, false, false>(a, stream);
-  return causal ? launch_one<64, 8, 64, true, false>(a, stream) : launch_one<64, 8, 64, false, false>(a, stream);
+  if (D == 128) return causal ? launch_one<128, 8, 64, true, false>(a, n_cu, stream) : launch_one<128, 8, 64, false, false>(a, n_cu, stream);
+  return causal ? launch_one<64, 8, 64, true, false>(a, n_cu, stream) : launch_one<64, 8, 64, false, false>(a, n_cu, stream);
 }
 
 }  // namespace tattn

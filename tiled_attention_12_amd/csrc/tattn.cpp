@@ -93,9 +93,10 @@ TATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, flo
   bool nothing = false;
   int st = check_mha(q, k, v, o, lse, B, H, Sq, Skv, D, causal, scale, &nothing);
   if (st != TATTN_OK || nothing) return st;
-  if ((st = have_device()) != TATTN_OK) return st;
+  int cus = 0;
+  if ((st = current_device_cus(&cus)) != TATTN_OK) return st;
   return status_of(tattn::launch_mha_fwd_bf16(q, k, v, o, lse, B, H, H, Sq, Skv, D, causal != 0, 0, nullptr,
-                                              scale, (hipStream_t)stream));
+                                              scale, cus, (hipStream_t)stream));
 }
 
 TATTN_API int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -108,9 +109,10 @@ TATTN_API int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   bool nothing = false;
   int st = check_mha(q, k, v, o, lse, B, H, Sq, Skv, D, causal, scale, &nothing);
   if (st != TATTN_OK || nothing) return st;
-  if ((st = have_device()) != TATTN_OK) return st;
+  int cus = 0;
+  if ((st = current_device_cus(&cus)) != TATTN_OK) return st;
   return status_of(tattn::launch_mha_fwd_bf16(q, k, v, o, lse, B, H, Hkv, Sq, Skv, D, causal != 0, window,
-                                              block_mask, scale, (hipStream_t)stream));
+                                              block_mask, scale, cus, (hipStream_t)stream));
 }
 
 TATTN_API int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
