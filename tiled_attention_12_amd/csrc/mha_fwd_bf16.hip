@@ -397,8 +397,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       int t_plain = Skv / BC;
       if (CAUSAL) t_plain = min(t_plain, max(0, (q0 + Skv - Sq + 1) / BC));
       t_plain = min(t_plain, nt);
-      // pipelined tiles: 0 .. t_main-1 with t_main = 1 + UN*k
-      const int t_main = t_plain >= 1 ? 1 + UN * ((t_plain - 1) / UN) : 0;
+      // pipelined tiles: 0 .. t_main-1 (every tile that needs no mask)
+      const int t_main = t_plain;
       if (t_main > 0) {
         wait_tile(0);
         wait_lgkmcnt0();
@@ -411,6 +411,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             constexpr int ST = U % NSTAGE, SP = (U - 1) % NSTAGE;
             constexpr int BN = U % 2, BP = (U - 1) % 2;
             const int t = t0 + U;
+            if (t >= t_main) return;  // the last pass may end early
             wait_tile(t);
             wait_lgkmcnt0();
             barrier();
@@ -437,10 +438,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             });
           });
         }
-        // tile t_main - 1 (= UN*k: stage 0, set 0) still needs its softmax and P*V
-        bf16x8 pf[KB][2];
-        vphase(t_main - 1, sb[0], pf, std::false_type{});
-        m2(std::integral_constant<int, 0>{}, pf);
+        // tile t_main - 1 still needs its softmax and P*V; its stage and
+        // score set follow from its position in the unrolled pass
+        const int r_last = (t_main - 1) % UN;
+        static_for<UN>([&](auto Rc) {
+          constexpr int R = decltype(Rc)::value;
+          if (r_last != R) return;
+          bf16x8 pf[KB][2];
+          vphase(t_main - 1, sb[R % 2], pf, std::false_type{});
+          m2(std::integral_constant<int, R % NSTAGE>{}, pf);
+        });
       }
 
       // the remaining tiles (causal diagonal, ragged tail) run masked, in order
