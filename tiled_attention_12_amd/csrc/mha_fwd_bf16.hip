@@ -48,7 +48,7 @@
 #endif
 // VALU instructions scheduled between consecutive score MFMAs
 #ifndef TATTN_VALU_PER_MFMA
-#define TATTN_VALU_PER_MFMA 4
+#define TATTN_VALU_PER_MFMA 3
 #endif
 
 
