@@ -148,16 +148,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // row half, K/V choice and stage are immediate offsets.
     const uint32_t smem0 = lds_addr(smem);
     uint32_t kbase[KS];
-  #pragma unroll
+#pragma unroll
     for (int ks = 0; ks < KS; ++ks) kbase[ks] = smem0 + col * RS + 16 * swz<CPR>(col, 2 * ks + hi);
     uint32_t vbase[2][DB];
     {
       const int gq = (lane >> 4) & 1, s16 = lane & 15;
       const int x = 2 * gq + ((s16 & 3) >> 1), boff = 8 * (s16 & 1);
-  #pragma unroll
+#pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int rr = 8 * e + 4 * hi + (s16 >> 2);
-  #pragma unroll
+#pragma unroll
         for (int db = 0; db < DB; ++db) vbase[e][db] = smem0 + VREG + rr * RS + 16 * swz<CPR>(rr, db * 4 + x) + boff;
       }
     }
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int lim = Skv - 1 - t * BC;  // >= 0: tile t has a visible key
       const char* kt = kp + (size_t)t * BC * RS;
       const char* vt = vp + (size_t)t * BC * RS;
-  #pragma unroll
+#pragma unroll
       for (int n = 0; n < LOADS; ++n) {
         const int slot = (n * NW + wave) * 64 + lane;
         const int row = slot / CPR;
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     bf16x8 qf[KS];
     {
       const int row = wrow0 + col;
-  #pragma unroll
+#pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         u32x4 x = {0, 0, 0, 0};
         if (row < Sq) x = *(const u32x4*)(qp + (size_t)row * D + ks * 16 + hi * 8);
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
 
     f32x16 oacc[DB];
-  #pragma unroll
+#pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     float m = -INFINITY, lsum = 0.f;
 
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     //   M1: S^T = K*Q^T (MFMA), V: masks + online softmax (VALU), M2: O^T += V^T*P^T (MFMA)
     auto m1 = [&](auto STc, f32x16 (&s)[KB]) {
       constexpr int ST = decltype(STc)::value;
-  #pragma unroll
+#pragma unroll
       for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16{};
       // k-steps in groups of 2; inside a group the key blocks alternate, so
       // consecutive MFMAs never depend on each other. The K fragments of group
@@ -256,18 +256,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             lo = pos - a.window;
           }
         }
-  #pragma unroll
+#pragma unroll
         for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = kv0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
             if (j > lim || j < lo) s[kb][i] = -INFINITY;
           }
       }
       float mx = -INFINITY;
-  #pragma unroll
+#pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
       mx = max_halves(mx) * c;
       const bool raise = mx - m > TAU;  // false when mx == -inf
@@ -275,19 +275,19 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const float alpha = raise ? fast_exp2(m - mx) : 1.f;
         m = raise ? mx : m;
         lsum *= alpha;
-  #pragma unroll
+#pragma unroll
         for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
       }
     };
     // V, second part: exponentials, row sums, P^T in bf16
     auto vexp = [&](const f32x16 (&s)[KB], bf16x8 (&pf)[KB][2]) {
       const float mc = m == -INFINITY ? 0.f : m;
-  #pragma unroll
+#pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-  #pragma unroll
+#pragma unroll
         for (int half = 0; half < 2; ++half) {
           float p[8];
-  #pragma unroll
+#pragma unroll
           for (int j = 0; j < 8; ++j) {
             p[j] = fast_exp2(fmaf(s[kb][half * 8 + j], c, -mc));
             lsum += p[j];
@@ -479,9 +479,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (row < Sq) {
         const float inv = l > 0.f ? 1.f / l : 0.f;
         uint16_t* orow = a.o + ((size_t)bh * Sq + row) * D;
-  #pragma unroll
+#pragma unroll
         for (int db = 0; db < DB; ++db)
-  #pragma unroll
+#pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int d = db * 32 + 8 * g4 + 4 * hi;
             u32x2 w = {pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv),
