@@ -346,3 +346,20 @@ def test_mla_calls_on_two_streams(ta, dev):
         assert torch.equal(xb[0], rb[0]) and torch.equal(xb[1], rb[1])
     ro, rl = oracle.mla_decode(*_mla_vals(mb), mb["indptr"], scale)
     assert_bf16_parity(to_np(rb[0]), to_np(rb[1]), ro, rl, "mla stream b")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_more_items_than_compute_units_without_xcd_order(ta, dev, causal):
+    # B*H = 5 is not a multiple of 8, so items are taken in plain order; 5 heads
+    # of 64 query tiles are 320 items, more than one pass of a 256-CU grid.
+    # Every row block of a few heads is checked on sampled rows.
+    B, H, S, D = 1, 5, 16384, 128
+    x = inputs.mha_inputs(B, H, S, S, D, seed=77)
+    o, lse = _run_mha(ta, dev, x, causal, 0.088)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rng = np.random.default_rng(78)
+    rows = np.unique(np.concatenate([np.arange(0, S, 256), np.arange(255, S, 256), rng.integers(0, S, 16)]))
+    for h in (0, 2, 4):
+        sl = lambda n: inputs.stored_values(x[n][:, h:h + 1])
+        ro, rl = oracle.attention(sl("q"), sl("k"), sl("v"), 0.088, causal=causal, rows=rows)
+        assert_bf16_parity(o[:, h:h + 1, rows], lse[:, h:h + 1, rows], ro, rl, f"H=5 S={S} causal={causal} h={h}")
