@@ -12,7 +12,10 @@
  * as void* (NULL selects the default stream of the current device). The
  * library never frees, retains or reallocates caller memory; outputs are
  * fully overwritten (never accumulated into). Calls are reentrant and may be
- * issued concurrently on different streams.
+ * issued concurrently on different streams. attn_fwd, attn_fwd_ex and
+ * attn_fwd_f32 allocate nothing and issue only kernel launches, so they may
+ * be captured into a HIP graph; mla_decode keeps a device workspace and
+ * orders calls with an event (see its description).
  *
  * bf16 tensors are raw IEEE bfloat16 bit patterns (uint16 storage). All
  * tensors are dense, row-major (last index fastest), with no padding.
