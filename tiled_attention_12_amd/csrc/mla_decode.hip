@@ -113,8 +113,11 @@ __global__ __launch_bounds__(1024) void mla_plan_kernel(MlaArgs a) {
 
 // Combine: one workgroup of 256 threads per (batch, 8 heads); thread t owns
 // head 8*blockIdx.y + t/32 and latent columns 16*(t%32) .. +15. Pieces of
-// empty slices between the two owners wrote nothing and are skipped.
+// empty slices between the two owners wrote nothing and are skipped. The
+// merge keeps a running maximum of the pieces' log-sum-exps, so the loads of
+// up to four pieces are issued together.
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a, int P) {
+  constexpr int MP = 4;
   const int b = blockIdx.x;
   const int H = a.H;
   const int h = blockIdx.y * 8 + (threadIdx.x >> 5);
@@ -130,28 +133,44 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a, int P) {
     return;
   }
   const int w0 = split_owner(g0, T, P), w1 = split_owner(g1 - 1, T, P);
-  float mx = -INFINITY;
-  for (int v = w0; v <= w1; ++v) {
-    if (split_start(v, T, P) == split_start(v + 1, T, P)) continue;
-    mx = fmaxf(mx, a.part_lse[((size_t)v + b) * H + h]);
-  }
+  float mx = -INFINITY, tot = 0.f;
   f32x4 acc[4] = {};
-  float tot = 0.f;
-  for (int v = w0; v <= w1; ++v) {
-    if (split_start(v, T, P) == split_start(v + 1, T, P)) continue;
-    const size_t slot = (size_t)v + b;
-    const float ls = a.part_lse[slot * H + h];
-    const float wt = ls == -INFINITY ? 0.f : __expf(ls - mx);
-    tot += wt;
-    const u32x4* src = (const u32x4*)(a.part_o + (slot * H + h) * kDl + c0);
+  for (int v0 = w0; v0 <= w1; v0 += MP) {
+    float ls[MP];
+    u32x4 x[MP][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const u32x4 x = src[i];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        acc[2 * i + k / 2][2 * (k % 2)] += wt * __uint_as_float(x[k] << 16);
-        acc[2 * i + k / 2][2 * (k % 2) + 1] += wt * __uint_as_float(x[k] & 0xffff0000u);
+    for (int k = 0; k < MP; ++k) {
+      const int v = v0 + k;
+      ls[k] = -INFINITY;
+      x[k][0] = x[k][1] = u32x4{0u, 0u, 0u, 0u};
+      if (v <= w1 && split_start(v, T, P) != split_start(v + 1, T, P)) {
+        const size_t slot = (size_t)v + b;
+        ls[k] = a.part_lse[slot * H + h];
+        const u32x4* src = (const u32x4*)(a.part_o + (slot * H + h) * kDl + c0);
+        x[k][0] = src[0];
+        x[k][1] = src[1];
       }
+    }
+    float mn = mx;
+#pragma unroll
+    for (int k = 0; k < MP; ++k) mn = fmaxf(mn, ls[k]);
+    if (mn == -INFINITY) continue;
+    const float sc = mx == -INFINITY ? 0.f : __expf(mx - mn);  // rescale of what was merged so far
+    tot *= sc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] *= sc;
+    mx = mn;
+#pragma unroll
+    for (int k = 0; k < MP; ++k) {
+      const float wt = ls[k] == -INFINITY ? 0.f : __expf(ls[k] - mx);
+      tot += wt;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * i + q / 2][2 * (q % 2)] += wt * __uint_as_float(x[k][i][q] << 16);
+          acc[2 * i + q / 2][2 * (q % 2) + 1] += wt * __uint_as_float(x[k][i][q] & 0xffff0000u);
+        }
     }
   }
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
