@@ -35,11 +35,19 @@ section):
   recorded in the design notes, and its identity with the unsplit result is
   pinned by the tests.
 
-Parity status: every function above is pinned by ``tests/test_oracle.py``
-(closed forms, invariants, a high-precision brute force on tiny inputs, an
+* ``ssd`` (submodule) -- the Mamba-2 state-space scan that the pages name as
+  their linear-attention workload (chunk-state and chunk-scan; "TileLang
+  paper summary", appendix A.4, and the tiled Mamba scan sketch of "From
+  FlashAttention to general kernels", section 4): the step-by-step
+  recurrence and its chunked form.
+
+Parity status: every function above is pinned by ``tests/test_oracle.py``,
+``tests/test_oracle_variants.py`` and ``tests/test_oracle_ssd.py`` (closed
+forms, invariants, a high-precision brute force on tiny inputs, an
 independent library routine). Nothing is "parity unpinned".
 """
 
+from . import ssd  # noqa: F401
 from .core import (  # noqa: F401
     attention,
     attention_masked,

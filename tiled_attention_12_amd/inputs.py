@@ -6,7 +6,8 @@ type. Both sides of a parity check consume exactly the stored values (bf16
 bits for the kernels, the same bits widened to float64 for the CPU side).
 
 Draw order is fixed so a seed names one input set: MHA draws Q, K, V; MLA
-draws (ragged lengths first, when asked for) Q, Q_pe, KV, K_pe. Each array is
+draws (ragged lengths first, when asked for) Q, Q_pe, KV, K_pe; the
+state-space scan draws x, B, C, dt, A and (when asked for) an initial state. Each array is
 float32 ``standard_normal`` times ``sigma`` (in float32), then rounded to
 bf16 with round-to-nearest-even when the storage type is bf16.
 """
@@ -103,3 +104,27 @@ def block_mask(B, H, Sq, Skv, density, seed, block=64):
     shape = (B, H, -(-Sq // block), -(-Skv // block))
     return (rng.random(shape) < density).astype(np.uint8)
 
+
+
+def ssd_inputs(Bt, L, H, G, P, N, seed, sigma=1.0, dt_range=(1e-3, 1e-1),
+               a_range=(1.0, 16.0), init_state=False, init_sigma=0.1):
+    """Inputs of the Mamba-2 state-space scan.
+
+    x [Bt, L, H, P], B and C [Bt, L, G, N]: bf16 bits of float32 normals times
+    ``sigma``. dt [Bt, L, H] float32, log-uniform on ``dt_range`` (the range
+    Mamba-2 initialises its step sizes to). A [H] float32, minus a uniform draw
+    on ``a_range`` (Mamba-2's A = -exp(A_log) initialisation). With
+    ``init_state``, an initial state [Bt, H, P, N] float32 of normals times
+    ``init_sigma``.
+    """
+    rng = np.random.default_rng(seed)
+    x = f32_to_bf16_bits(_draw(rng, (Bt, L, H, P), sigma))
+    b = f32_to_bf16_bits(_draw(rng, (Bt, L, G, N), sigma))
+    c = f32_to_bf16_bits(_draw(rng, (Bt, L, G, N), sigma))
+    lo, hi = np.log(dt_range[0]), np.log(dt_range[1])
+    dt = np.exp(rng.uniform(lo, hi, size=(Bt, L, H))).astype(np.float32)
+    a = (-rng.uniform(a_range[0], a_range[1], size=H)).astype(np.float32)
+    out = {"x": x, "B": b, "C": c, "dt": dt, "A": a}
+    if init_state:
+        out["init_state"] = _draw(rng, (Bt, H, P, N), init_sigma)
+    return out
