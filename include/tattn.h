@@ -12,10 +12,10 @@
  * as void* (NULL selects the default stream of the current device). The
  * library never frees, retains or reallocates caller memory; outputs are
  * fully overwritten (never accumulated into). Calls are reentrant and may be
- * issued concurrently on different streams. attn_fwd, attn_fwd_ex and
- * attn_fwd_f32 allocate nothing and issue only kernel launches, so they may
- * be captured into a HIP graph; mla_decode keeps a device workspace and
- * orders calls with an event (see its description).
+ * issued concurrently on different streams. attn_fwd, attn_fwd_ex,
+ * attn_fwd_f32 and ssd_scan allocate nothing and issue only kernel launches,
+ * so they may be captured into a HIP graph; mla_decode keeps a device
+ * workspace and orders calls with an event (see its description).
  *
  * bf16 tensors are raw IEEE bfloat16 bit patterns (uint16 storage). All
  * tensors are dense, row-major (last index fastest), with no padding.
@@ -25,7 +25,10 @@
  * the attention definition S = Q*K^T, P = softmax(S), O = P*V and the
  * online-softmax recurrence; "TileLang programming model and FlashMLA"
  * (sections 2.1-2.2, 3.1) gives the MLA decode kernel with its exp2 softmax
- * and running log-sum.
+ * and running log-sum. The state-space scan (ssd_scan) is the Mamba-2
+ * chunk-state / chunk-scan workload named in "TileLang paper summary"
+ * (appendix A.4) and sketched as a tiled scan in "From FlashAttention to
+ * general kernels" (section 4).
  */
 #ifndef TATTN_H
 #define TATTN_H
@@ -159,6 +162,47 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 int mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe,
                void* o, float* lse, int B, int H, const int32_t* kv_indptr,
                float scale, void* stream);
+
+/*
+ * ssd_scan -- Mamba-2 state-space scan (chunk state, state passing and chunk
+ * scan fused into one pass), bf16 in and out, fp32 state.
+ *
+ * The linear-attention workload of "TileLang paper summary" (appendix A.4:
+ * Mamba-2's chunk-scan and chunk-state functions), walked in chunks of 64
+ * steps like the tiled Mamba scan of "From FlashAttention to general
+ * kernels" (section 4). For every batch b < batch and head h < heads, with
+ * group g = h / (heads / groups) and state S (headdim x dstate, fp32):
+ *   S_t = exp(dt[b,t,h] * A[h]) * S_{t-1} + dt[b,t,h] * x[b,t,h,:] (outer) B[b,t,g,:]
+ *   y[b,t,h,:] = S_t * C[b,t,g,:]
+ * for t = 0 .. seqlen-1, starting from S_{-1} = init_state[b,h] (zero when
+ * init_state is NULL). The scan runs chunk by chunk: inside a chunk the
+ * outputs come from one causal, decay-weighted product against the chunk's
+ * own steps plus the decayed entering state; the state then advances by the
+ * chunk's contribution. The state never leaves the GPU between chunks.
+ *
+ *   x           device bf16 [batch, seqlen, heads, headdim]
+ *   dt          device fp32 [batch, seqlen, heads], step sizes (> 0 in
+ *               Mamba-2; any finite value is accepted and used as given)
+ *   A           device fp32 [heads], decay rates (< 0 in Mamba-2)
+ *   B, C        device bf16 [batch, seqlen, groups, dstate]
+ *   y           device bf16 [batch, seqlen, heads, headdim], written
+ *   init_state  device fp32 [batch, heads, headdim, dstate] or NULL
+ *   final_state device fp32 [batch, heads, headdim, dstate] or NULL; when
+ *               given, receives S_{seqlen-1} (init_state, or zero, when
+ *               seqlen == 0). It must not overlap init_state.
+ *   batch, seqlen, heads >= 0; groups >= 1 dividing heads (else
+ *               TATTN_ERR_INVALID_ARG)
+ *   headdim     64, dstate 128 (else TATTN_ERR_UNSUPPORTED)
+ * Alignment: x, B, C, y, init_state and final_state 16 bytes, dt and A 4
+ * bytes (else TATTN_ERR_ALIGN). batch * seqlen * heads * headdim must stay
+ * below 2^62 elements and batch * heads below 2^31 (else
+ * TATTN_ERR_UNSUPPORTED). y is rounded to bf16 once, at the end; the state
+ * enters the products with C as bf16, and the decay-weighted B of a chunk
+ * enters the state update as bf16, like the reference Mamba-2 kernels.
+ */
+int ssd_scan(const void* x, const float* dt, const float* A, const void* B, const void* C, void* y,
+             const float* init_state, float* final_state, int batch, int seqlen, int heads,
+             int groups, int headdim, int dstate, void* stream);
 
 /* Static, NUL-terminated description of a status code ("unknown status"
  * for a value that is not one of the codes above). Never returns NULL. */

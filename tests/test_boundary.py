@@ -20,7 +20,8 @@ def _header_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert _header_symbols() == ["attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "tattn_status_str"]
+    assert _header_symbols() == ["attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "ssd_scan",
+                                 "tattn_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib_path):
@@ -105,6 +106,30 @@ def test_mla_argument_validation(L):
     assert call(B=0, q=None) == OK
 
 
+def test_ssd_argument_validation(L):
+    def call(x=16, dt=4, A=4, B=16, C=16, y=16, s0=None, s1=None, Bt=2, Ls=100, H=8, G=1, P=64, N=128):
+        return L.ssd_scan(x, dt, A, B, C, y, s0, s1, Bt, Ls, H, G, P, N, None)
+    assert call(x=None) == INVALID
+    assert call(A=None) == INVALID
+    assert call(y=None) == INVALID
+    assert call(Bt=-1) == INVALID
+    assert call(Ls=-1) == INVALID
+    assert call(G=0) == INVALID
+    assert call(G=3) == INVALID            # 8 heads do not split into 3 groups
+    assert call(P=128) == UNSUP
+    assert call(N=64) == UNSUP
+    assert call(x=24) == ALIGN
+    assert call(B=8) == ALIGN
+    assert call(dt=2) == ALIGN
+    assert call(s0=32, s1=40) == ALIGN
+    # final state overlapping the initial state
+    assert call(s0=4096, s1=4096 + 64 * 128 * 4) == INVALID
+    assert call(Bt=0, x=None, dt=None, A=None, B=None, C=None, y=None) == OK
+    assert call(H=0, G=0, x=None) == OK
+    # no steps and no final state: nothing to do
+    assert call(Ls=0, x=None, dt=None, B=None, C=None, y=None) == OK
+
+
 def test_valid_request_without_gpu_is_a_hip_error(lib_path):
     """Run in a child process that hides every GPU, so the answer is the
     no-device path on any host."""
@@ -116,12 +141,13 @@ def test_valid_request_without_gpu_is_a_hip_error(lib_path):
         "r2=L.attn_fwd_f32(16,16,16,16,16,1,1,8,8,64,1,F(0.1),None);"
         "r3=L.mla_decode(16,16,16,16,16,16,2,128,16,F(0.1),None);"
         "r4=L.attn_fwd_ex(16,16,16,16,16,1,4,1,8,8,128,1,3,None,F(0.1),None);"
-        "print(r1,r2,r3,r4)"
+        "r5=L.ssd_scan(16,16,16,16,16,16,None,None,1,64,2,1,64,128,None);"
+        "print(r1,r2,r3,r4,r5)"
     )
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1")
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
     assert out.returncode == 0, out.stderr
-    assert out.stdout.split() == [str(HIP)] * 4
+    assert out.stdout.split() == [str(HIP)] * 5
 
 
 def test_status_strings_cover_every_code(L):

@@ -1,0 +1,160 @@
+"""GPU parity of ssd_scan (the Mamba-2 state-space scan) against the CPU
+float64 oracle (needs gfx950).
+
+Element by element at sizes the oracle finishes quickly (several 64-step
+chunks and ragged tails, both workgroup shapes: two heads per workgroup when
+heads per group is even, one when it is odd), with and without initial and
+final states; on sampled heads at the full benchmark workload.
+
+Tolerance. The kernel rounds to bf16 at four points, as the reference
+Mamba-2 kernels do: the decay-weighted scores G inside a chunk, the
+decay-weighted B of the state update, the state where it meets C, and y
+itself. Each rounding is a relative error of at most 2^-9 on one term of a
+sum of up to 64 + 128 terms, so the error of y is a small multiple of 2^-9
+times the size of those terms, which is the size of y itself. The bound is
+|dy| <= 2^-8 |y| + 2^-5 rms(y) per element (rms over the head's outputs)
+and mean |dy| <= 2^-8 rms(y); for the fp32 final state, which only sees the
+rounding of B, the same form with the state's rms.
+"""
+
+import numpy as np
+import pytest
+
+import oracle.ssd as ossd
+from tests.helpers import to_dev, to_np
+from tiled_attention_12_amd import inputs
+from tiled_attention_12_amd.workloads import WORKLOADS
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+REL, ABS_RMS, MEAN_RMS = 2.0 ** -8, 2.0 ** -5, 2.0 ** -8
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ta(lib_path):
+    import tiled_attention_12_amd as ta
+    return ta
+
+
+def _ref_inputs(d):
+    return (inputs.stored_values(d["x"]), d["dt"], d["A"], inputs.stored_values(d["B"]),
+            inputs.stored_values(d["C"]))
+
+
+def _run(ta, dev, d, final=False):
+    x, B, C = (to_dev(d[n], dev) for n in ("x", "B", "C"))
+    dt, A = to_dev(d["dt"], dev), to_dev(d["A"], dev)
+    s0 = to_dev(d["init_state"], dev) if "init_state" in d else None
+    r = ta.ssd_scan(x, dt, A, B, C, init_state=s0, final_state=final)
+    torch.cuda.synchronize()
+    if final:
+        return to_np(r[0]), to_np(r[1])
+    return to_np(r), None
+
+
+def _check(got, ref, what, axis_rows):
+    """got/ref [..., rows ...]: per-slice rms over `axis_rows` axes."""
+    err = np.abs(got - ref)
+    rms = np.sqrt(np.mean(ref ** 2, axis=axis_rows, keepdims=True))
+    bound = REL * np.abs(ref) + ABS_RMS * rms
+    worst = (err - bound).max() if err.size else 0.0
+    mean_ratio = (err.mean(axis=axis_rows, keepdims=True) / np.maximum(rms, 1e-30)).max() if err.size else 0.0
+    msg = f"{what}: max|d|={err.max() if err.size else 0:.3g} worst excess={worst:.3g} mean/rms={mean_ratio:.3g}"
+    print(msg, flush=True)
+    assert worst <= 0, msg
+    assert mean_ratio <= MEAN_RMS, msg
+
+
+CASES = [
+    # Bt, L, H, G, init, final
+    (2, 200, 4, 1, True, True),      # two heads per workgroup, ragged tail, states in and out
+    (2, 130, 6, 2, True, True),      # three heads per group: one head per workgroup
+    (1, 64, 8, 4, False, True),      # exactly one chunk, four groups
+    (3, 65, 2, 1, False, False),     # 3 workgroups (no XCD order), one step in the last chunk
+    (1, 1, 2, 2, True, True),        # a single step; one head per group
+    (2, 63, 2, 1, True, True),
+    (4, 700, 16, 2, False, True),    # 32 workgroups, 11 chunks
+]
+
+
+@pytest.mark.parametrize("Bt,L,H,G,init,final", CASES)
+def test_ssd_against_oracle(ta, dev, Bt, L, H, G, init, final):
+    d = inputs.ssd_inputs(Bt, L, H, G, 64, 128, seed=7000 + L + H, init_state=init)
+    print(f"ssd Bt={Bt} L={L} H={H} G={G} init={init} final={final}", flush=True)
+    y, f = _run(ta, dev, d, final)
+    ry, rf = ossd.ssd_chunked(*_ref_inputs(d), 64, d.get("init_state"))
+    _check(y.transpose(0, 2, 1, 3), ry.transpose(0, 2, 1, 3), "y", (2, 3))
+    if final:
+        _check(f, rf, "final state", (2, 3))
+
+
+def test_ssd_empty_sequence_copies_the_state(ta, dev):
+    d = inputs.ssd_inputs(2, 0, 4, 1, 64, 128, seed=7100, init_state=True)
+    y, f = _run(ta, dev, d, final=True)
+    assert y.shape == (2, 0, 4, 64)
+    np.testing.assert_array_equal(f, d["init_state"].astype(np.float64))
+    d.pop("init_state")
+    _, f = _run(ta, dev, d, final=True)
+    assert not f.any()
+
+
+def test_ssd_extreme_decay_rates(ta, dev):
+    # fastest decay of the Mamba-2 range (dt = 0.1, A = -16: the state forgets
+    # within a step or two and exp underflows inside a chunk) next to almost
+    # no decay over a long sequence (dt = 1e-3, A = -1)
+    d = inputs.ssd_inputs(1, 1000, 4, 1, 64, 128, seed=7200, init_state=True)
+    d["dt"][:, :, :2] = 0.1
+    d["dt"][:, :, 2:] = 1e-3
+    d["A"][:2] = -16.0
+    d["A"][2:] = -1.0
+    y, f = _run(ta, dev, d, final=True)
+    ry, rf = ossd.ssd_chunked(*_ref_inputs(d), 64, d["init_state"])
+    _check(y.transpose(0, 2, 1, 3), ry.transpose(0, 2, 1, 3), "y", (2, 3))
+    _check(f, rf, "final state", (2, 3))
+
+
+def test_ssd_full_workload_sampled_heads(ta, dev):
+    w = WORKLOADS["ssd_scan_bf16"]
+    d = inputs.ssd_inputs(w["Bt"], w["L"], w["H"], w["G"], w["P"], w["N"], seed=w["seed"])
+    print(f"ssd full workload {w}", flush=True)
+    y, f = _run(ta, dev, d, final=True)
+    rng = np.random.default_rng(5)
+    pairs = [(0, 0), (w["Bt"] - 1, w["H"] - 1)] + [(int(rng.integers(w["Bt"])), int(rng.integers(w["H"])))
+                                                    for _ in range(6)]
+    ry, rf = ossd.ssd_rows(*_ref_inputs(d), pairs, 64)
+    for i, (b, h) in enumerate(pairs):
+        _check(y[b, :, h][None], ry[i][None], f"y b={b} h={h}", (1, 2))
+        _check(f[b, h][None], rf[i][None], f"final state b={b} h={h}", (1, 2))
+
+
+def test_ssd_more_heads_than_one_pass_of_the_chip(ta, dev):
+    # 16 x 80 heads (a 2.7B-class layer): 640 workgroups of two heads
+    d = inputs.ssd_inputs(16, 256, 80, 1, 64, 128, seed=7300)
+    y, _ = _run(ta, dev, d)
+    pairs = [(0, 0), (15, 79), (7, 40), (3, 1), (12, 63)]
+    ry, _ = ossd.ssd_rows(*_ref_inputs(d), pairs, 64)
+    for i, (b, h) in enumerate(pairs):
+        _check(y[b, :, h][None], ry[i][None], f"y b={b} h={h}", (1, 2))
+
+
+def test_ssd_continuation_matches_one_pass(ta, dev):
+    # the final state of the first half, fed back as the initial state of the
+    # second half, gives the one-pass outputs of the second half
+    d = inputs.ssd_inputs(2, 320, 4, 1, 64, 128, seed=7400, init_state=True)
+    y, f = _run(ta, dev, d, final=True)
+    L1 = 192
+    first = {k: (v[:, :L1] if k in ("x", "B", "C", "dt") else v) for k, v in d.items()}
+    _, f1 = _run(ta, dev, first, final=True)
+    second = {k: (v[:, L1:] if k in ("x", "B", "C", "dt") else v) for k, v in d.items()}
+    second["init_state"] = f1.astype(np.float32)
+    y2, f2 = _run(ta, dev, second, final=True)
+    _check(y2.transpose(0, 2, 1, 3), y[:, L1:].transpose(0, 2, 1, 3), "second half y", (2, 3))
+    _check(f2, f, "final state", (2, 3))

@@ -19,7 +19,7 @@ TATTN_ERR_ALIGN = -3
 TATTN_ERR_OOM = -4
 TATTN_ERR_HIP = -5
 
-EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "tattn_status_str")
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "ssd_scan", "tattn_status_str")
 
 
 class TattnError(RuntimeError):
@@ -45,6 +45,8 @@ def _load():
     lib.attn_fwd_ex.restype = i32
     lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, f32, vp]
     lib.mla_decode.restype = i32
+    lib.ssd_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    lib.ssd_scan.restype = i32
     lib.tattn_status_str.argtypes = [i32]
     lib.tattn_status_str.restype = ctypes.c_char_p
     return lib
@@ -188,3 +190,44 @@ def mla_decode(q, q_pe, kv, k_pe, kv_indptr, scale, out=None, lse=None, stream=N
     if rc != TATTN_OK:
         raise TattnError(rc, "mla_decode")
     return out, lse
+
+
+def ssd_scan(x, dt, A, B, C, init_state=None, final_state=False, out=None, stream=None):
+    """Mamba-2 state-space scan: x [Bt,L,H,64] bf16, dt [Bt,L,H] fp32, A [H] fp32,
+    B and C [Bt,L,G,128] bf16, optional init_state [Bt,H,64,128] fp32.
+    Returns y bf16 [Bt,L,H,64], and with ``final_state`` (True, or an fp32
+    [Bt,H,64,128] tensor to fill) also the state after the last step."""
+    torch = _torch()
+    if x.dim() != 4 or dt.dim() != 3 or A.dim() != 1 or B.dim() != 4 or C.dim() != 4:
+        raise ValueError("x [Bt,L,H,P], dt [Bt,L,H], A [H], B/C [Bt,L,G,N]")
+    Bt, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(dt.shape) != (Bt, L, H) or tuple(A.shape) != (H,) or tuple(B.shape) != (Bt, L, G, N) \
+            or tuple(C.shape) != (Bt, L, G, N):
+        raise ValueError("dt/A/B/C shapes do not match x")
+    dev = x.device
+    for n, t, dty in (("x", x, torch.bfloat16), ("dt", dt, torch.float32), ("A", A, torch.float32),
+                      ("B", B, torch.bfloat16), ("C", C, torch.bfloat16)):
+        _check_dev(n, t, dty, dev)
+    if init_state is not None:
+        _check_dev("init_state", init_state, torch.float32, dev)
+        if tuple(init_state.shape) != (Bt, H, P, N):
+            raise ValueError("init_state must be [Bt, H, P, N]")
+    fs = None
+    if final_state is True:
+        fs = torch.empty((Bt, H, P, N), dtype=torch.float32, device=dev)
+    elif final_state is not False and final_state is not None:
+        fs = final_state
+        _check_dev("final_state", fs, torch.float32, dev)
+        if tuple(fs.shape) != (Bt, H, P, N):
+            raise ValueError("final_state must be [Bt, H, P, N]")
+    if out is None:
+        out = torch.empty_like(x)
+    _check_dev("out", out, torch.bfloat16, dev)
+    if tuple(out.shape) != (Bt, L, H, P):
+        raise ValueError("out has the wrong shape")
+    rc = _LIB.ssd_scan(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(out), _ptr(init_state), _ptr(fs),
+                       Bt, L, H, G, P, N, _stream_ptr(dev, stream))
+    if rc != TATTN_OK:
+        raise TattnError(rc, "ssd_scan")
+    return (out, fs) if fs is not None else out

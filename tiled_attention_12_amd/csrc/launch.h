@@ -27,4 +27,11 @@ hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, co
                              void* o, float* lse, int B, int H, const int32_t* kv_indptr,
                              float scale, int n_split, void* workspace, hipStream_t stream);
 
+// Mamba-2 state-space scan: x [Bt, L, H, 64] bf16, dt [Bt, L, H] fp32,
+// A [H] fp32, B/C [Bt, L, G, 128] bf16 -> y [Bt, L, H, 64] bf16; the initial
+// and final states [Bt, H, 64, 128] fp32 may be null.
+hipError_t launch_ssd_scan_bf16(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                                void* y, const float* init_state, float* final_state, int Bt, int L, int H,
+                                int G, hipStream_t stream);
+
 }  // namespace tattn

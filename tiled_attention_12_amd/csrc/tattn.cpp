@@ -176,6 +176,32 @@ TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const 
   return status_of(er);
 }
 
+TATTN_API int ssd_scan(const void* x, const float* dt, const float* A, const void* B, const void* C, void* y,
+                       const float* init_state, float* final_state, int batch, int seqlen, int heads,
+                       int groups, int headdim, int dstate, void* stream) {
+  if (batch < 0 || seqlen < 0 || heads < 0 || groups < 0 || headdim < 0 || dstate < 0)
+    return TATTN_ERR_INVALID_ARG;
+  if (heads > 0 && (groups < 1 || heads % groups != 0)) return TATTN_ERR_INVALID_ARG;
+  if (headdim != 64 || dstate != 128) return TATTN_ERR_UNSUPPORTED;
+  if (batch == 0 || heads == 0) return TATTN_OK;
+  if (seqlen == 0 && !final_state) return TATTN_OK;
+  if (!A || (seqlen > 0 && (!x || !dt || !B || !C || !y))) return TATTN_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) || !aligned(init_state, 16) ||
+      !aligned(final_state, 16) || !aligned(dt, 4) || !aligned(A, 4))
+    return TATTN_ERR_ALIGN;
+  if ((long long)batch * heads > INT_MAX) return TATTN_ERR_UNSUPPORTED;
+  if ((double)batch * seqlen * heads * headdim >= 4.6e18) return TATTN_ERR_UNSUPPORTED;
+  if (final_state && init_state) {
+    const uintptr_t bytes = (uintptr_t)batch * heads * headdim * dstate * 4;
+    const uintptr_t f = (uintptr_t)final_state, i = (uintptr_t)init_state;
+    if (f < i + bytes && i < f + bytes) return TATTN_ERR_INVALID_ARG;
+  }
+  int st = have_device();
+  if (st != TATTN_OK) return st;
+  return status_of(tattn::launch_ssd_scan_bf16(x, dt, A, B, C, y, init_state, final_state, batch, seqlen,
+                                               heads, groups, (hipStream_t)stream));
+}
+
 TATTN_API const char* tattn_status_str(int status) {
   switch (status) {
     case TATTN_OK: return "ok";

@@ -1,4 +1,4 @@
-"""The five reference workloads: shapes, distributions, seeds.
+"""The benchmark workloads: shapes, distributions, seeds.
 
 Workload i (1-based) draws its inputs from seed 1000 + i. ``scale`` is the
 float32 value passed to the kernels; the CPU side widens that same float32.
@@ -32,6 +32,9 @@ WORKLOADS = {
     "mha_blocksparse_bf16": dict(kind="mha", dtype="bf16", B=4, H=16, Sq=4096, Skv=4096, D=128,
                                  causal=(False,), density=0.5, sigma=1.0, scale=F32_SCALE_128,
                                  seed=1008),
+    # Mamba-2 state-space scan (chunk state + chunk scan), a 1.3B-class layer:
+    # 64 heads of width 64, state 128, one B/C group
+    "ssd_scan_bf16": dict(kind="ssd", Bt=8, L=4096, H=64, G=1, P=64, N=128, seed=1009),
 }
 
 
@@ -84,3 +87,23 @@ def mla_flops(H, total_keys, Dl=512, Dr=64):
 def mla_bytes(B, H, total_keys, Dl=512, Dr=64):
     """Algorithmic HBM bytes: KV and K_pe rows, Q and Q_pe read once; O (bf16) and LSE written."""
     return 2 * (Dl + Dr) * int(total_keys) + 2 * B * H * (Dl + Dr) + 2 * B * H * Dl + 4 * B * H
+
+
+def ssd_bytes(Bt, L, H, G, P, N, init_state=False, final_state=False):
+    """Algorithmic HBM bytes of the scan: x, B, C (bf16), dt (fp32) and A read
+    once, y (bf16) written once, fp32 initial / final states when used."""
+    b = 2 * Bt * L * H * P * 2 + 2 * Bt * L * G * N * 2 + 4 * Bt * L * H + 4 * H
+    b += 4 * Bt * H * P * N * (int(bool(init_state)) + int(bool(final_state)))
+    return b
+
+
+def ssd_flops(Bt, L, H, P, N, chunk=64):
+    """FLOPs of the chunked form's products: per chunk of q steps, C*B^T and
+    the decay-weighted product with x over the causal pairs (q(q+1)/2 each),
+    the entering state against C and the state update (q*P*N each)."""
+    full, tail = divmod(L, chunk)
+    macs = 0
+    for q, n in ((chunk, full), (tail, 1 if tail else 0)):
+        pairs = q * (q + 1) // 2
+        macs += n * (pairs * (N + P) + 2 * q * P * N)
+    return 2 * Bt * H * macs
