@@ -3,8 +3,8 @@
 One step = one pass of the prefill hot path over the headline workload
 (bf16 MHA B=4, H=16, Sq=Skv=2048, D=128), run once non-causal and once
 causal. The long causal prefill (B=1, H=32, S=16384), the attention variants
-(grouped KV heads, sliding window, block mask) and the two MLA decode
-workloads are measured in the same run and reported under "workloads".
+(grouped KV heads, sliding window, block mask), the two MLA decode
+workloads and the Mamba-2 state-space scan are measured in the same run and reported under "workloads".
 Inputs are seeded synthetic draws, resident in HBM before timing; each
 workload rotates three input copies so consecutive launches read cold data.
 
@@ -145,6 +145,14 @@ def _mla_workload(ta, dev, name):
     return w, sets, total
 
 
+def _ssd_workload(ta, dev, name="ssd_scan_bf16"):
+    from tiled_attention_12_amd import inputs
+    from tiled_attention_12_amd.workloads import WORKLOADS
+    w = WORKLOADS[name]
+    x = inputs.ssd_inputs(w["Bt"], w["L"], w["H"], w["G"], w["P"], w["N"], seed=w["seed"])
+    return w, _copies(x, dev)
+
+
 def _cpu_baseline(budget_s=12.0):
     """The CPU oracle, as it stands, on a bounded sample of the headline
     workload: whole (batch, head) slices, non-causal and causal alternately,
@@ -185,6 +193,11 @@ def _profile_only(args, ta, dev):
         w, sets = _mha_workload(ta, dev, name.replace("_causal", "") if name == "mha_prefill_bf16_causal" else name)
         o, l = ta.attn_fwd(sets[0]["q"], sets[0]["k"], sets[0]["v"], causal=causal, scale=w["scale"])
         fn = lambda s: ta.attn_fwd(s["q"], s["k"], s["v"], causal=causal, scale=w["scale"], out=o, lse=l)
+    elif name.startswith("ssd"):
+        w, sets = _ssd_workload(ta, dev, name)
+        s0 = sets[0]
+        y = ta.ssd_scan(s0["x"], s0["dt"], s0["A"], s0["B"], s0["C"])
+        fn = lambda s: ta.ssd_scan(s["x"], s["dt"], s["A"], s["B"], s["C"], out=y)
     else:
         w, sets, _ = _mla_workload(ta, dev, name)
         s0 = sets[0]
@@ -203,7 +216,7 @@ def main():
                     help="only the headline prefill workload (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["mha_prefill_bf16", "mha_prefill_bf16_causal", "mha_long_causal_bf16",
-                                       "mla_decode_bf16", "mla_decode_ragged_bf16"],
+                                       "mla_decode_bf16", "mla_decode_ragged_bf16", "ssd_scan_bf16"],
                     help="profiling mode: run --steps launches of one workload, print its timing only")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="profiling mode: first run one device-to-device copy of this many MiB "
@@ -216,7 +229,7 @@ def main():
 
     import torch
     import tiled_attention_12_amd as ta
-    from tiled_attention_12_amd.workloads import mha_bytes, mha_flops, mla_bytes, mla_flops
+    from tiled_attention_12_amd.workloads import mha_bytes, mha_flops, mla_bytes, mla_flops, ssd_bytes, ssd_flops
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -343,6 +356,21 @@ def main():
                                "tflops": fl / (mean_m * 1e-3) / 1e12,
                                "frac_roofline": t_star / (mean_m * 1e-3)}
             del setsm, om, lm
+
+        _log("bench: ssd_scan_bf16")
+        ws, setss = _ssd_workload(ta, dev)
+        s0 = setss[0]
+        ys = ta.ssd_scan(s0["x"], s0["dt"], s0["A"], s0["B"], s0["C"])
+        mean_s, med_s, min_s = _time_launches(
+            lambda s: ta.ssd_scan(s["x"], s["dt"], s["A"], s["B"], s["C"], out=ys), setss, 3, 20)
+        fl = ssd_flops(ws["Bt"], ws["L"], ws["H"], ws["P"], ws["N"])
+        by = ssd_bytes(ws["Bt"], ws["L"], ws["H"], ws["G"], ws["P"], ws["N"])
+        t_star = max(by / (PEAK_HBM_GBS * 1e9), fl / (PEAK_BF16_TFLOPS * 1e12))
+        workloads["ssd_scan_bf16"] = {"ms": mean_s, "ms_median": med_s, "ms_min": min_s,
+                                      "alg_gbs": by / (mean_s * 1e-3) / 1e9,
+                                      "tflops": fl / (mean_s * 1e-3) / 1e12,
+                                      "frac_roofline": t_star / (mean_s * 1e-3)}
+        del setss, ys
 
     achieved = f_nc / (nc_ms * 1e-3) / 1e12
     line = {
