@@ -243,14 +243,15 @@ def test_mla_ragged_batch_equals_standalone(ta, dev):
     assert_bf16_parity(o, lse, ro, rl, "mla ragged 4")
 
 
+@pytest.mark.parametrize("H", [32, 128])
 @pytest.mark.parametrize("B", [1023, 1100])
-def test_mla_many_batches(ta, dev, B):
+def test_mla_many_batches(ta, dev, B, H):
     # below 1024 batches the split kernel forms the tile prefix itself; from
     # 1024 on a separate plan launch does: both paths, with empty batches
     rng = np.random.default_rng(B)
     lens = rng.integers(0, 4, size=B)
     lens[::7] = 0
-    m = inputs.mla_inputs(B, 32, seed=B + 1, kv_len=1)
+    m = inputs.mla_inputs(B, H, seed=B + 1, kv_len=1)
     indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     n = int(indptr[-1])
     g = np.random.default_rng(B + 2)
@@ -262,7 +263,7 @@ def test_mla_many_batches(ta, dev, B):
     ro, rl = oracle.mla_decode(*_mla_vals(m), indptr, scale)
     empty = lens == 0
     assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
-    assert_bf16_parity(o, lse, ro, rl, f"mla B={B}")
+    assert_bf16_parity(o, lse, ro, rl, f"mla B={B} H={H}")
 
 
 def test_mla_deterministic(ta, dev):
