@@ -439,20 +439,32 @@ void mla_split_kernel(MlaArgs a) {
       }
     }
 
-    // ---- normalised partial of this piece -> slot (workgroup + batch)
+    // ---- normalised partial of this piece -> slot (workgroup + batch). The
+    // rows go through LDS (the ring is free once every wave has passed the
+    // barrier below) so that each store writes one whole 1 KB head row.
     {
       const float l = sum_halves(lsum);
       const float inv = l > 0.f ? 1.f / l : 0.f;
       const size_t slot = (size_t)w + b;
-      uint16_t* po = a.part_o + (slot * H + head) * kDl;
+      constexpr int SRS = kDl * 2 + 16;  // staging row stride (padded)
+      static_assert(NW * 32 * SRS <= NSTAGE * kStage, "staging fits the ring");
+      typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+      typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+      const uint32_t stg = lds_addr(smem) + wave * 32 * SRS;
+      barrier();
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const int d = db * 32 + 8 * g4 + 4 * hi;
-          *(u32x2*)(po + d) = u32x2{pack_bf16x2(oacc[db][g4 * 4] * inv, oacc[db][g4 * 4 + 1] * inv),
-                                    pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
+          *(lds_u32x2*)(uintptr_t)(stg + col * SRS + d * 2) =
+              u32x2{pack_bf16x2(oacc[db][g4 * 4] * inv, oacc[db][g4 * 4 + 1] * inv),
+                    pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
         }
+      uint16_t* po = a.part_o + (slot * H + wave * 32) * kDl + 8 * lane;
+#pragma unroll 8
+      for (int r = 0; r < 32; ++r)
+        *(u32x4*)(po + (size_t)r * kDl) = *(const lds_u32x4*)(uintptr_t)(stg + r * SRS + 16 * lane);
       if (hi == 0) a.part_lse[slot * H + head] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
 
