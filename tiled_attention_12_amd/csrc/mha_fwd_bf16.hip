@@ -472,24 +472,43 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     }
 
-    // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2
+    // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2. The
+    // wave's 32 rows go through LDS (the ring is free once every wave has
+    // passed the barrier below) so each store writes whole, contiguous rows.
     {
       const float l = sum_halves(lsum);
       const int row = wrow0 + col;
-      if (row < Sq) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
-        uint16_t* orow = a.o + ((size_t)bh * Sq + row) * D;
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      constexpr int SRS = RS + 16;  // staging row stride (padded)
+      static_assert(NW * 32 * SRS <= 2 * NSTAGE * TILE, "staging fits the ring");
+      typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+      typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+      // (addresses from an opaque copy of the lane id, so the compiler does
+      // not compute them before the tile loop and hold them across it)
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const uint32_t stg = lds_addr(smem) + wave * 32 * SRS;
+      const uint32_t wr = stg + (ln & 31) * SRS + 8 * (ln >> 5);
+      barrier();
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int d = db * 32 + 8 * g4 + 4 * hi;
-            u32x2 w = {pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv),
-                       pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
-            *(u32x2*)(orow + d) = w;
-          }
-        if (hi == 0) a.lse[(size_t)bh * Sq + row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int d = db * 32 + 8 * g4;
+          *(lds_u32x2*)(uintptr_t)(wr + d * 2) =
+              u32x2{pack_bf16x2(oacc[db][g4 * 4 + 0] * inv, oacc[db][g4 * 4 + 1] * inv),
+                    pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
+        }
+      // each store: 64 lanes x 16 bytes = 64 / CPR whole rows
+      constexpr int RPS = 64 / CPR;
+      const int rsub = ln / CPR, csub = ln % CPR;
+#pragma unroll
+      for (int r0 = 0; r0 < 32; r0 += RPS) {
+        const int rr = r0 + rsub;
+        const u32x4 v = *(const lds_u32x4*)(uintptr_t)(stg + rr * SRS + 16 * csub);
+        if (wrow0 + rr < Sq) *(u32x4*)(a.o + ((size_t)bh * Sq + wrow0 + rr) * D + 8 * csub) = v;
       }
+      if (row < Sq && hi == 0) a.lse[(size_t)bh * Sq + row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
   };
 
