@@ -91,8 +91,8 @@ __device__ __forceinline__ void load_lds4_asm(const void* gptr, uint32_t lds_bas
                :: "v"(gptr), "s"(lds_base_uniform) : "memory", "m0");
 }
 
-__device__ __forceinline__ void store8_asm(void* gptr, u32x2 v) {
-  asm volatile("global_store_dwordx2 %0, %1, off" :: "v"(gptr), "v"(v) : "memory");
+__device__ __forceinline__ void store16_asm(void* gptr, u32x4 v) {
+  asm volatile("global_store_dwordx4 %0, %1, off" :: "v"(gptr), "v"(v) : "memory");
 }
 
 // bf16 pair * (c0, c1), rounded back to bf16
@@ -224,9 +224,10 @@ __global__ __launch_bounds__(256 * TEAMS) void ssd_scan_bf16_kernel(SsdArgs a) {
     const int ST = c & 1;
     const uint32_t stg = smem0 + ST * Lds::STAGE;
     const int t0 = c * kQ;
-    // chunk c's loads have landed once only the previous chunk's 4 y stores
-    // may still be in flight (vector memory operations complete in order)
-    if (c == 0) wait_vmcnt<0>(); else wait_vmcnt<4>();
+    // chunk c's loads have landed once only the previous chunk's (at most 2)
+    // y stores may still be in flight (vector memory operations complete in
+    // order)
+    if (c == 0) wait_vmcnt<0>(); else wait_vmcnt<2>();
     wait_lgkmcnt0();
     barrier();
     if (c + 1 < nc) issue(c + 1, ST ^ 1);
@@ -335,17 +336,28 @@ __global__ __launch_bounds__(256 * TEAMS) void ssd_scan_bf16_kernel(SsdArgs a) {
         }
       };
       if (ypb) pv(std::integral_constant<int, 1>{}); else pv(std::integral_constant<int, 0>{});
-      char* yrow = (char*)a.y + (((size_t)b * L + t0 + t) * H + h) * (kP * 2) + (32 * ypb + 4 * hh) * 2;
-      const bool full = t0 + kQ <= L;
+      // The wave's 32x32 block of y goes through the team's x tile of this
+      // stage (no wave reads it after the barrier that follows the state
+      // update; the next loads into this stage wait for the barrier at the
+      // top of the next chunk), rows [t][p] with 16-byte chunk c of row t at
+      // position c ^ (t & 7); each store then writes 64-byte row pieces. A
+      // wave reads back only its own block, so no barrier is needed here.
+      typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+      typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+      const uint32_t ys = stg + Lds::XOFF + team * (kQ * kP * 2);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const u32x2 v = {pack_bf16x2(yacc[4 * j], yacc[4 * j + 1]),
-                         pack_bf16x2(yacc[4 * j + 2], yacc[4 * j + 3])};
-        if (full) {
-          store8_asm(yrow + 16 * j, v);
-        } else if (t0 + t < L) {
-          *(u32x2*)(yrow + 16 * j) = v;
-        }
+        const int cch = 4 * ypb + j;
+        *(lds_u32x2*)(uintptr_t)(ys + t * (kP * 2) + 16 * (cch ^ (t & 7)) + 8 * hh) =
+            u32x2{pack_bf16x2(yacc[4 * j], yacc[4 * j + 1]), pack_bf16x2(yacc[4 * j + 2], yacc[4 * j + 3])};
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int tr = 32 * ytb + 16 * k + (lane >> 2);
+        const int cc = 4 * ypb + (lane & 3);
+        const u32x4 v = *(const lds_u32x4*)(uintptr_t)(ys + tr * (kP * 2) + 16 * (cc ^ (tr & 7)));
+        if (t0 + tr < L)
+          store16_asm((char*)a.y + (((size_t)b * L + t0 + tr) * H + h) * (kP * 2) + 16 * cc, v);
       }
     }
     write_state();
