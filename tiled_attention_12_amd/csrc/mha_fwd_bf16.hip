@@ -196,9 +196,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       wait_vmcnt<0>();
     };
 
-    // Q^T fragments (B operand), loaded once.
+    // Q^T fragments (B operand), loaded once. On the dense path the wave's
+    // 32 rows first come into LDS, whole rows per load, through ring stages
+    // 1 and 2 (unused until the first barrier of the item: K side for the
+    // first half of the waves, V side for the rest), laid out like a K tile
+    // so the fragment reads use the K-operand addresses. Rows past Sq repeat
+    // row Sq - 1; their results are never written.
     bf16x8 qf[KS];
-    {
+    if constexpr (!EXT && PF == 1) {
+      const uint32_t qb = smem0 + (wave < NW / 2 ? TILE + wave * (32 * RS) : VREG + TILE + (wave - NW / 2) * (32 * RS));
+      constexpr int QL = 32 * CPR / 64;
+#pragma unroll
+      for (int n = 0; n < QL; ++n) {
+        const int slot = n * 64 + lane;
+        const int r = slot / CPR;
+        const int grow = min(wrow0 + r, Sq - 1);
+        load_lds16_asm((const char*)(qp + (size_t)grow * D) + 16 * swz<CPR>(r, slot % CPR), qb + n * 1024);
+      }
+      wait_vmcnt<0>();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = as_bf16x8(lds_read128((const void*)(uintptr_t)(kbase[ks] - smem0 + qb)));
+    } else {
       const int row = wrow0 + col;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
