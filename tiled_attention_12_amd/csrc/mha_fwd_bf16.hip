@@ -196,14 +196,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       wait_vmcnt<0>();
     };
 
-    // Q^T fragments (B operand), loaded once. On the dense path the wave's
-    // 32 rows first come into LDS, whole rows per load, through ring stages
-    // 1 and 2 (unused until the first barrier of the item: K side for the
-    // first half of the waves, V side for the rest), laid out like a K tile
-    // so the fragment reads use the K-operand addresses. Rows past Sq repeat
-    // row Sq - 1; their results are never written.
+    // Q^T fragments (B operand), loaded once. The wave's 32 rows first come
+    // into LDS, whole rows per load, through ring stages 1 and 2 (unused
+    // until the first barrier of the item: K side for the first half of the
+    // waves, V side for the rest), laid out like a K tile so the fragment
+    // reads use the K-operand addresses. Rows past Sq repeat row Sq - 1;
+    // their results are never written.
     bf16x8 qf[KS];
-    if constexpr (!EXT && PF == 1) {
+    constexpr bool QSTAGE = PF == 1;
+    auto load_q_staged = [&]() {
       const uint32_t qb = smem0 + (wave < NW / 2 ? TILE + wave * (32 * RS) : VREG + TILE + (wave - NW / 2) * (32 * RS));
       constexpr int QL = 32 * CPR / 64;
 #pragma unroll
@@ -218,6 +219,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
         qf[ks] = as_bf16x8(lds_read128((const void*)(uintptr_t)(kbase[ks] - smem0 + qb)));
+    };
+    if constexpr (QSTAGE) {
+      // the window/mask path stages Q after issuing its first tile
+      if constexpr (!EXT) load_q_staged();
     } else {
       const int row = wrow0 + col;
 #pragma unroll
@@ -379,7 +384,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       f32x16 sx[KB];
       int cur = t_first;
       if (cur < t_end && !active(cur)) cur = next_active(cur);
-      if (cur < t_end) issue(cur, std::integral_constant<int, 0>{});
+      if (cur < t_end) {
+        issue(cur, std::integral_constant<int, 0>{});
+        if constexpr (QSTAGE) load_q_staged();
+      }
       for (int cnt = 0; cur < t_end; ++cnt) {
         // mask bytes are read before the next refill is issued, so waiting for
         // them never waits for that refill
