@@ -11,7 +11,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 sys.path.insert(0, ROOT)
 
-from tiled_attention_12_amd.workloads import mha_bytes, mha_flops, mla_bytes, mla_flops  # noqa: E402
+from tiled_attention_12_amd.workloads import (mha_bytes, mha_flops, mla_bytes, mla_flops, ssd_bytes,  # noqa: E402
+                                              ssd_flops)
 
 
 @pytest.mark.parametrize("Sq,Skv", [(1, 1), (5, 5), (7, 3), (3, 7), (64, 200)])
@@ -35,6 +36,31 @@ def test_byte_counts():
     # MLA: 576-wide bf16 key rows, 576-wide queries, 512-wide bf16 outputs, fp32 LSE
     assert mla_bytes(64, 128, 262144) == 1152 * 262144 + 1152 * 64 * 128 + 1024 * 64 * 128 + 4 * 64 * 128
     assert mla_flops(128, 10) == 2 * 128 * 1088 * 10
+
+
+def test_ssd_byte_count_of_the_scan_workload():
+    # x and y bf16 [8, 4096, 64, 64]; B and C bf16 [8, 4096, 1, 128]; dt fp32 [8, 4096, 64]; A fp32 [64]
+    xy = 8 * 4096 * 64 * 64 * 2
+    bc = 8 * 4096 * 1 * 128 * 2
+    assert ssd_bytes(8, 4096, 64, 1, 64, 128) == 2 * xy + 2 * bc + 8 * 4096 * 64 * 4 + 64 * 4 == 562036992
+    # fp32 states [Bt, H, P, N] in and out
+    assert ssd_bytes(2, 10, 4, 2, 64, 128, True, True) - ssd_bytes(2, 10, 4, 2, 64, 128) == 2 * 2 * 4 * 64 * 128 * 4
+
+
+@pytest.mark.parametrize("L", [1, 63, 64, 65, 200])
+def test_ssd_flops_brute_force(L):
+    # per (batch, head) and chunk of q steps: C_t . B_s over the pairs s <= t (N each), the decay-weighted
+    # product with x over the same pairs (P each), the entering state against C (q*P*N) and the state
+    # update (q*P*N); two flops per multiply-add
+    Bt, H, P, N, Q = 2, 3, 5, 7, 64
+    macs = 0
+    for c0 in range(0, L, Q):
+        q = min(Q, L - c0)
+        for t in range(q):
+            for s in range(t + 1):
+                macs += N + P
+        macs += 2 * q * P * N
+    assert ssd_flops(Bt, L, H, P, N) == 2 * Bt * H * macs
 
 
 def test_more_than_one_gpu_is_refused():
