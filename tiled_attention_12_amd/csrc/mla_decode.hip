@@ -79,12 +79,10 @@ __device__ __forceinline__ int split_start(int w, int T, int P) {
   return (int)(((long long)w * T) / P);
 }
 
-// The workgroup whose slice holds global tile g (0 <= g < T).
+// The workgroup whose slice holds global tile g (0 <= g < T): the largest w
+// with floor(w*T/P) <= g, i.e. w*T < (g+1)*P, i.e. ceil((g+1)*P/T) - 1.
 __device__ __forceinline__ int split_owner(int g, int T, int P) {
-  int w = (int)(((long long)g * P) / T);
-  while (w + 1 < P && split_start(w + 1, T, P) <= g) ++w;
-  while (w > 0 && split_start(w, T, P) > g) --w;
-  return w;
+  return (int)((((long long)g + 1) * P - 1) / T);
 }
 
 __global__ __launch_bounds__(1024) void mla_plan_kernel(MlaArgs a) {
@@ -133,6 +131,17 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a, int P) {
     return;
   }
   const int w0 = split_owner(g0, T, P), w1 = split_owner(g1 - 1, T, P);
+  // Slice v covers tiles [floor(v*T/P), floor((v+1)*T/P)); the bounds are
+  // stepped from w0 as v*T = q*P + r (T = tq*P + tr), so no slice costs a
+  // division (these are wave-uniform, and 64-bit divisions on the shared
+  // scalar unit had made this kernel scalar-bound).
+  const int tq = T / P, tr = T - tq * P;
+  int q, r;
+  {
+    const long long vt = (long long)w0 * T;
+    q = (int)(vt / P);
+    r = (int)(vt - (long long)q * P);
+  }
   float mx = -INFINITY, tot = 0.f;
   f32x4 acc[4] = {};
   for (int v0 = w0; v0 <= w1; v0 += MP) {
@@ -141,9 +150,17 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a, int P) {
 #pragma unroll
     for (int k = 0; k < MP; ++k) {
       const int v = v0 + k;
+      int q1 = q + tq, r1 = r + tr;
+      if (r1 >= P) {
+        r1 -= P;
+        ++q1;
+      }
+      const bool nonempty = q1 != q;  // floor((v+1)*T/P) != floor(v*T/P)
+      q = q1;
+      r = r1;
       ls[k] = -INFINITY;
       x[k][0] = x[k][1] = u32x4{0u, 0u, 0u, 0u};
-      if (v <= w1 && split_start(v, T, P) != split_start(v + 1, T, P)) {
+      if (v <= w1 && nonempty) {
         const size_t slot = (size_t)v + b;
         ls[k] = a.part_lse[slot * H + h];
         const u32x4* src = (const u32x4*)(a.part_o + (slot * H + h) * kDl + c0);
