@@ -534,7 +534,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int r0 = 0; r0 < 32; r0 += RPS) {
         const int rr = r0 + rsub;
         const u32x4 v = *(const lds_u32x4*)(uintptr_t)(stg + rr * SRS + 16 * csub);
-        if (wrow0 + rr < Sq) *(u32x4*)(a.o + ((size_t)bh * Sq + wrow0 + rr) * D + 8 * csub) = v;
+        // streaming stores: the output is not read again by this kernel
+        if (wrow0 + rr < Sq)
+          __builtin_nontemporal_store(v, (u32x4*)(a.o + ((size_t)bh * Sq + wrow0 + rr) * D + 8 * csub));
       }
       if (row < Sq && hi == 0) a.lse[(size_t)bh * Sq + row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }

@@ -91,8 +91,9 @@ __device__ __forceinline__ void load_lds4_asm(const void* gptr, uint32_t lds_bas
                :: "v"(gptr), "s"(lds_base_uniform) : "memory", "m0");
 }
 
+// streaming (non-temporal) 16-byte store: y is not read again by the scan
 __device__ __forceinline__ void store16_asm(void* gptr, u32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off" :: "v"(gptr), "v"(v) : "memory");
+  asm volatile("global_store_dwordx4 %0, %1, off nt" :: "v"(gptr), "v"(v) : "memory");
 }
 
 // bf16 pair * (c0, c1), rounded back to bf16
