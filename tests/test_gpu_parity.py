@@ -145,6 +145,20 @@ def test_bf16_row_shift_invariance(ta, dev):
     assert np.abs((l2 - l1) - c).max() <= 2e-3
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_key_permutation_invariance(ta, dev, D):
+    # non-causal attention is a sum over keys: permuting K and V rows together
+    # (across tiles and the ragged tail) changes O only by rounding order
+    x = inputs.mha_inputs(2, 3, 200, 333, D, seed=14)
+    perm = np.random.default_rng(15).permutation(333)
+    moved = dict(x, k=np.ascontiguousarray(x["k"][:, :, perm]), v=np.ascontiguousarray(x["v"][:, :, perm]))
+    o1, l1 = _run_mha(ta, dev, x, False, 0.1)
+    o2, l2 = _run_mha(ta, dev, moved, False, 0.1)
+    assert np.abs(o1 - o2).max() <= 1e-2
+    assert np.abs(l1 - l2).max() <= 1e-3
+    assert np.linalg.norm(o1 - o2) <= 1e-2 * np.linalg.norm(o1)
+
+
 def test_bf16_deterministic(ta, dev):
     x = inputs.mha_inputs(2, 4, 300, 300, 128, seed=13)
     a = _run_mha(ta, dev, x, True, 0.088)
@@ -264,6 +278,27 @@ def test_mla_many_batches(ta, dev, B, H):
     empty = lens == 0
     assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
     assert_bf16_parity(o, lse, ro, rl, f"mla B={B} H={H}")
+
+
+def test_mla_key_permutation_invariance(ta, dev):
+    # permuting each batch's key rows (latent and rotary together) moves keys
+    # across tiles, splits and the ragged tail; O changes only by rounding
+    lens = [700, 1500, 33]
+    m = inputs.mla_inputs(len(lens), 128, seed=24, kv_len=1)
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    g = np.random.default_rng(25)
+    n = int(indptr[-1])
+    m["kv"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 512), dtype=np.float32) * np.float32(0.3))
+    m["k_pe"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 64), dtype=np.float32) * np.float32(0.3))
+    m["indptr"] = indptr
+    perm = np.concatenate([indptr[b] + g.permutation(L) for b, L in enumerate(lens)])
+    moved = dict(m, kv=np.ascontiguousarray(m["kv"][perm]), k_pe=np.ascontiguousarray(m["k_pe"][perm]))
+    scale = float(np.float32(576 ** -0.5))
+    o1, l1 = _run_mla(ta, dev, m, scale)
+    o2, l2 = _run_mla(ta, dev, moved, scale)
+    assert np.abs(o1 - o2).max() <= 1e-2
+    assert np.abs(l1 - l2).max() <= 1e-3
+    assert np.linalg.norm(o1 - o2) <= 1e-2 * np.linalg.norm(o1)
 
 
 def test_mla_deterministic(ta, dev):
