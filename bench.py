@@ -335,10 +335,18 @@ def main():
                     pairs = sum(visible_pairs(wv["Sq"], wv["Skv"], causal, window, mask_np[b, h])
                                 for b in range(wv["B"]) for h in range(wv["H"]))
                 fv = 2 * pairs * 2 * wv["D"]
+                # Q, K, V read once, O and LSE written once, the mask read once
+                bv = mha_bytes(wv["B"], wv["H"], wv["Sq"], wv["Skv"], wv["D"], 2, Hkv=wv.get("Hkv"))
+                if mask_np is not None:
+                    bv += mask_np.size
+                t_hbm, t_mfma = bv / (PEAK_HBM_GBS * 1e9), fv / (PEAK_BF16_TFLOPS * 1e12)
                 key = f"{name}_{'causal' if causal else 'noncausal'}"
                 workloads[key] = {"ms": mean_v, "ms_median": med_v, "ms_min": min_v, "visible_pairs": pairs,
                                   "tflops": fv / (mean_v * 1e-3) / 1e12,
-                                  "frac_mfma_peak": fv / (mean_v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+                                  "frac_mfma_peak": fv / (mean_v * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                                  "alg_gbs": bv / (mean_v * 1e-3) / 1e9,
+                                  "bound": "hbm" if t_hbm > t_mfma else "mfma",
+                                  "frac_roofline": max(t_hbm, t_mfma) / (mean_v * 1e-3)}
             del setsv, ov, lv, mask_dev
 
         for name in ("mla_decode_bf16", "mla_decode_ragged_bf16"):

@@ -113,3 +113,21 @@ def test_visible_pairs_brute_force(Sq, Skv, causal, W):
                  if (not causal or j <= i + Skv - Sq) and (W == 0 or i + Skv - Sq - W <= j < i + Skv - Sq + W)
                  and (mask is None or mask[i // 64, j // 64]))
         assert visible_pairs(Sq, Skv, causal, W, mask) == bf
+
+
+def test_window_workload_is_hbm_bound_and_block_mask_mfma_bound():
+    """The sliding window (256 keys per row over 8192) moves more bytes per
+    FLOP than the ridge of 8 TB/s against 2516.6 TFLOP/s allows, so its
+    roofline is HBM; the half-dense block mask stays on the MFMA side."""
+    from tiled_attention_12_amd.workloads import WORKLOADS, visible_pairs
+    w = WORKLOADS["mha_window_bf16"]
+    B, H, S, D = w["B"], w["H"], w["Sq"], w["D"]
+    by = mha_bytes(B, H, S, S, D, 2)
+    assert by == 2 * 4 * B * H * S * D + 4 * B * H * S
+    fl = 4 * D * B * H * visible_pairs(S, S, True, w["window"])
+    assert fl == 4 * D * B * H * sum(min(i, w["window"]) + 1 for i in range(S))
+    assert by / 8000e9 > fl / 2516.6e12
+    m = WORKLOADS["mha_blocksparse_bf16"]
+    by_m = mha_bytes(m["B"], m["H"], m["Sq"], m["Skv"], m["D"], 2)
+    fl_m = 4 * m["D"] * m["B"] * m["H"] * m["Sq"] * m["Skv"] * m["density"]
+    assert by_m / 8000e9 < fl_m / 2516.6e12
