@@ -67,11 +67,12 @@ def test_sliding_window(ta, dev, D, causal, W, sq, skv):
     assert_bf16_parity(o, lse, ro, rl, f"window W={W} D={D} causal={causal} {sq}x{skv}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("density", [0.3, 0.7])
 @pytest.mark.parametrize("sq,skv", [(257, 300), (600, 600), (100, 700)])
-def test_block_mask(ta, dev, causal, density, sq, skv):
-    x = inputs.mha_inputs(2, 2, sq, skv, 128, seed=980 + sq + int(10 * density))
+def test_block_mask(ta, dev, D, causal, density, sq, skv):
+    x = inputs.mha_inputs(2, 2, sq, skv, D, seed=980 + sq + int(10 * density))
     mask = inputs.block_mask(2, 2, sq, skv, density, seed=981 + sq)
     o, lse = _run(ta, dev, x, causal, 0.088, mask=mask)
     ro, rl = oracle.attention_masked(*_vals(x, "qkv"), 0.088, causal=causal, block_mask=mask)
@@ -79,6 +80,19 @@ def test_block_mask(ta, dev, causal, density, sq, skv):
     assert np.array_equal(np.isneginf(lse), np.isneginf(rl))
     assert np.all(o[np.isneginf(rl)] == 0)
     assert_bf16_parity(o, lse, ro, rl, f"block mask d={density} causal={causal} {sq}x{skv}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_mask_grouped_heads_and_more_items_than_one_pass(ta, dev, causal):
+    # 4*16 heads of five 256-row query tiles each: more work items than the
+    # chip has compute units, in the XCD order (heads a multiple of 8), 4
+    # query heads per KV head
+    x = inputs.mha_inputs(4, 16, 1100, 1000, 128, seed=985, Hkv=4)
+    mask = inputs.block_mask(4, 16, 1100, 1000, 0.4, seed=986)
+    o, lse = _run(ta, dev, x, causal, 0.088, mask=mask)
+    ro, rl = oracle.attention_masked(*_vals(x, "qkv"), 0.088, causal=causal, block_mask=mask)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rl))
+    assert_bf16_parity(o, lse, ro, rl, f"block mask gqa many items causal={causal}")
 
 
 @pytest.mark.parametrize("causal", [False, True])
