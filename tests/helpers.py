@@ -54,13 +54,28 @@ def bf16_o_bound(ro):
     return BF16_MAX_ABS_O + np.where(np.abs(ro) >= 2.0, bf16_half_ulp(ro), 0.0)
 
 
+def bf16_round(x):
+    """Round to the nearest bf16 value, ties to even (through float32)."""
+    b = np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32).astype(np.uint64)
+    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def bf16_mean_o_bound(ro):
+    """Bound on mean |dO| for a bf16 output: 1e-3 beyond the mean error of
+    rounding the exact result itself to bf16. Where rows see a handful of
+    keys (tiny windows), |O| ~ 1 and that rounding alone averages ~2^-10."""
+    ro = np.asarray(ro, dtype=np.float64)
+    return BF16_MEAN_ABS_O + (float(np.abs(bf16_round(ro) - ro).mean()) if ro.size else 0.0)
+
+
 def assert_bf16_parity(o, lse, ro, rl, what=""):
     st = parity_stats(o, lse, ro, rl)
     msg = f"{what}: {st}"
     if st["max_o"] > BF16_MAX_ABS_O:  # only elements with |O| >= 2 may exceed 1e-2
         excess = np.abs(o - ro) - bf16_o_bound(ro)
         assert excess.max() <= 0, msg + f" (worst excess over the bf16 bound {excess.max():.3g})"
-    assert st["mean_o"] <= BF16_MEAN_ABS_O, msg
+    assert st["mean_o"] <= bf16_mean_o_bound(ro), msg
     assert st["max_lse"] <= BF16_MAX_ABS_LSE, msg
     assert st["rel_l2"] <= BF16_REL_L2_O, msg
     return st

@@ -131,3 +131,16 @@ def test_window_workload_is_hbm_bound_and_block_mask_mfma_bound():
     by_m = mha_bytes(m["B"], m["H"], m["Sq"], m["Skv"], m["D"], 2)
     fl_m = 4 * m["D"] * m["B"] * m["H"] * m["Sq"] * m["Skv"] * m["density"]
     assert by_m / 8000e9 < fl_m / 2516.6e12
+
+
+def test_bf16_round_ties_to_even_and_mean_bound():
+    from tests.helpers import BF16_MEAN_ABS_O, bf16_mean_o_bound, bf16_round
+    # halfway cases go to the even significand; others to the nearest
+    vals = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -9, -(1 + 2 ** -8), 2 ** -130, 0.0])
+    assert list(bf16_round(vals)) == [1.0, 1 + 2 ** -6, 1.0, -1.0, 2 ** -130, 0.0]
+    # exactly representable outputs leave the plain 1e-3 gate; |O| near 1
+    # adds the mean rounding error, below half an ulp (2^-9)
+    assert bf16_mean_o_bound(np.array([0.5, -0.25, 1.0])) == BF16_MEAN_ABS_O
+    r = np.random.default_rng(3).uniform(1.0, 2.0, 10000)
+    extra = bf16_mean_o_bound(r) - BF16_MEAN_ABS_O
+    assert 2 ** -10 * 0.9 < extra < 2 ** -9

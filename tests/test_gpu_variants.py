@@ -69,6 +69,19 @@ def test_sliding_window(ta, dev, D, causal, W, sq, skv):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("W", [385, 900])
+def test_wide_sliding_window(ta, dev, D, causal, W):
+    # wider than 768 visible keys per row (non-causal 2W, causal W + 1) or
+    # not: both workgroup shapes of the window walk, with ragged tails
+    x = inputs.mha_inputs(1, 3, 1300, 1250, D, seed=960 + W + D + int(causal))
+    scale = float(np.float32(D ** -0.5))
+    o, lse = _run(ta, dev, x, causal, scale, window=W)
+    ro, rl = oracle.attention_masked(*_vals(x, "qkv"), scale, causal=causal, window=W)
+    assert_bf16_parity(o, lse, ro, rl, f"wide window W={W} D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("density", [0.3, 0.7])
 @pytest.mark.parametrize("sq,skv", [(257, 300), (600, 600), (100, 700)])
 def test_block_mask(ta, dev, D, causal, density, sq, skv):
@@ -96,13 +109,14 @@ def test_block_mask_grouped_heads_and_more_items_than_one_pass(ta, dev, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_all_variants_together(ta, dev, causal):
+@pytest.mark.parametrize("W", [150, 800])
+def test_all_variants_together(ta, dev, causal, W):
     x = inputs.mha_inputs(2, 6, 520, 610, 128, seed=990, Hkv=2)
     mask = inputs.block_mask(2, 6, 520, 610, 0.6, seed=991)
-    o, lse = _run(ta, dev, x, causal, 0.09, window=150, mask=mask)
-    ro, rl = oracle.attention_masked(*_vals(x, "qkv"), 0.09, causal=causal, window=150, block_mask=mask)
+    o, lse = _run(ta, dev, x, causal, 0.09, window=W, mask=mask)
+    ro, rl = oracle.attention_masked(*_vals(x, "qkv"), 0.09, causal=causal, window=W, block_mask=mask)
     assert np.array_equal(np.isneginf(lse), np.isneginf(rl))
-    assert_bf16_parity(o, lse, ro, rl, f"gqa+window+mask causal={causal}")
+    assert_bf16_parity(o, lse, ro, rl, f"gqa+window W={W}+mask causal={causal}")
 
 
 def test_masked_out_everything(ta, dev):

@@ -33,8 +33,9 @@
 //    2^8 (in base-2 units), so the O rescale runs on few tiles; every
 //    exponential stays <= 2^8 and the result is unchanged (both O and l are
 //    taken relative to the same m).
-//  * Persistent grid: one workgroup per compute unit loops over work items
-//    (one 256-row query tile of one (batch, head) each). The hardware hands
+//  * Persistent grid: one workgroup per compute unit (two for the 4-wave
+//    narrow-window launch) loops over work items (one NW*32-row query tile of
+//    one (batch, head) each). The hardware hands
 //    workgroup i to XCD i % 8 and item i runs on XCD i % 8 too: all query
 //    tiles of a (batch, head) go to one XCD so its K/V stays in that XCD's
 //    L2. Causal items are taken longest first, and each workgroup's passes
@@ -105,9 +106,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int hi = lane >> 5;      // wave half
   const int col = lane & 31;     // query column owned by the lane
 
-  // One work item = one (batch*head, 256-row query tile). The grid is
-  // persistent (at most one workgroup per compute unit); item i runs where
-  // workgroup i would: on XCD i % 8.
+  // One work item = one (batch*head, BR-row query tile). The grid is
+  // persistent (as many workgroups as fit on the compute units at once);
+  // item i runs where workgroup i would: on XCD i % 8.
   auto process = [&](const int i) {
     int bh, qt;
     {
@@ -374,7 +375,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       auto active = [&](int t) {
         if (!mrow) return true;
         int any = 0;
-        for (int qb = qb_first; qb <= qb_last; ++qb) any |= mrow[qb * a.nkb + t];
+        for (int qb = qb_first; qb <= qb_last; ++qb) any |= mrow[qb * a.nkb + t * BC / kMaskBlock];
         return any != 0;
       };
       auto next_active = [&](int t) {
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         // them never waits for that refill
         const int nxt = next_active(cur);
         const bool wact = wave_rows && cur * BC < whi && (cur + 1) * BC > wlo &&
-                          (!mrow || mrow[qb_w * a.nkb + cur] != 0);
+                          (!mrow || mrow[qb_w * a.nkb + cur * BC / kMaskBlock] != 0);
         const int st = cnt % NSTAGE;
         static_for<NSTAGE>([&](auto STc) {
           constexpr int ST = decltype(STc)::value;
@@ -582,9 +583,12 @@ static hipError_t launch_one(const MhaArgs& a, int n_cu, hipStream_t stream) {
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   b.n_items = (int)items;
   b.remap = (a.n_bh % 8) == 0 && n_cu >= 8;
-  // one workgroup per compute unit (LDS and registers allow no second one);
-  // a multiple of 8 for the XCD order
-  long long grid = items < n_cu ? items : n_cu;
+  // as many workgroups per compute unit as LDS and two waves per SIMD allow
+  // (one for 8-wave workgroups); a multiple of 8 for the XCD order
+  constexpr int OCC = (int)(160 * 1024 / lds) < 8 / NW ? (int)(160 * 1024 / lds) : 8 / NW;
+  static_assert(OCC >= 1, "one workgroup must fit");
+  const long long slots = (long long)n_cu * OCC;
+  long long grid = items < slots ? items : slots;
   if (b.remap) grid = (grid / 8) * 8;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(NW * 64), lds, stream, b);
   return hipGetLastError();
@@ -610,6 +614,17 @@ hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void
   a.nqb = (Sq + kMaskBlock - 1) / kMaskBlock;
   a.nkb = (Skv + kMaskBlock - 1) / kMaskBlock;
   const bool ext = window > 0 || block_mask != nullptr;
+  // Narrow windows (at most 768 visible keys per row) run on 4-wave
+  // workgroups of 128 rows with 32-key tiles, two per compute unit, so one
+  // workgroup's loads, item start and output stores overlap the other's
+  // arithmetic; such a window moves more bytes per FLOP than the MFMAs need.
+  // Wider windows and block masks alone keep the 8-wave, 64-key walk.
+  const long long span = causal ? (long long)window + 1 : 2LL * window;
+  if (window > 0 && span <= 768) {
+    static_assert(kMaskBlock % 32 == 0, "mask blocks hold whole 32-key tiles");
+    if (D == 128) return causal ? launch_one<128, 4, 32, true, true>(a, n_cu, stream) : launch_one<128, 4, 32, false, true>(a, n_cu, stream);
+    return causal ? launch_one<64, 4, 32, true, true>(a, n_cu, stream) : launch_one<64, 4, 32, false, true>(a, n_cu, stream);
+  }
   if (ext) {
     if (D == 128) return causal ? launch_one<128, 8, 64, true, true>(a, n_cu, stream) : launch_one<128, 8, 64, false, true>(a, n_cu, stream);
     return causal ? launch_one<64, 8, 64, true, true>(a, n_cu, stream) : launch_one<64, 8, 64, false, true>(a, n_cu, stream);
