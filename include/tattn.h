@@ -80,10 +80,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              void* stream);
 
 /*
- * attn_fwd_ex -- attn_fwd with the attention variants of "TileLang study
- * notes", section 5.1 (other attention variants): grouped or single KV heads
- * (multi-query), a sliding key window (local attention) and a block mask
- * (sparse attention). With Hkv == H, window == 0 and block_mask == NULL it
+ * attn_fwd_ex -- attn_fwd with the attention variants of "TileLang
+ * programming model and FlashMLA", section 5.1 (other attention variants):
+ * grouped or single KV heads (multi-query), a sliding key window (local
+ * attention) and a block mask (sparse attention). With Hkv == H, window == 0 and block_mask == NULL it
  * computes exactly what attn_fwd computes.
  *
  *   k, v       device, bf16 [B, Hkv, Skv, D]; query head h reads KV head

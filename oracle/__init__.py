@@ -25,7 +25,7 @@ section):
   "Online Softmax" subsection states it. It is used only to check that the
   recurrence reaches the two-pass result.
 * ``attention_masked`` / ``visible_keys`` -- the attention variants of
-  "TileLang study notes", section 5.1: grouped and single KV heads
+  "TileLang programming model and FlashMLA", section 5.1: grouped and single KV heads
   (multi-query), a sliding key window around the query position, and a
   block mask that decides which (query block, key block) pairs are
   computed. Same definition as ``attention`` over each row's visible keys.

@@ -177,8 +177,8 @@ def visible_keys(i, Sq, Skv, causal=False, window=0, block_row=None, block=64):
     Key j is visible when 0 <= j < Skv and, with off = Skv - Sq (the
     bottom-right alignment used for the causal rule),
       * causal: j <= i + off;
-      * window W > 0: i + off - W <= j < i + off + W. "TileLang study notes",
-        section 5.1 (local attention), makes a sliding window by running the
+      * window W > 0: i + off - W <= j < i + off + W. "TileLang programming
+        model and FlashMLA", section 5.1 (local attention), makes a sliding window by running the
         key loop over the positions from the query position minus the window
         size up to (not including) the query position plus the window size;
       * block mask: block_row[j // block] != 0, where ``block_row`` is the
@@ -205,7 +205,8 @@ def attention_masked(q, k, v, scale, causal=False, window=0, block_mask=None, bl
     row's visible keys, O = P*V, natural-log LSE), with the visible set of
     ``visible_keys``. KV heads are shared by groups of query heads as in
     ``attention`` (query head h reads KV head h // (H // Hkv)); with one KV
-    head this is the multi-query form of "TileLang study notes", section 5.1.
+    head this is the multi-query form of "TileLang programming model and
+    FlashMLA", section 5.1.
     ``block_mask`` is [B, H, ceil(Sq/block), ceil(Skv/block)] (nonzero =
     computed) or None. A row that sees no key gets O = 0 and LSE = -inf.
     """

@@ -70,6 +70,10 @@ def bf16_mean_o_bound(ro):
 
 
 def assert_bf16_parity(o, lse, ro, rl, what=""):
+    """bf16 parity for the edge and variant cases, where rows that see a
+    handful of keys may exceed 1e-2 by the bf16 half-ulp of an exact |O| >= 2
+    (bf16_o_bound, bf16_mean_o_bound); the five benchmark configurations use
+    assert_config_parity instead."""
     st = parity_stats(o, lse, ro, rl)
     msg = f"{what}: {st}"
     if st["max_o"] > BF16_MAX_ABS_O:  # only elements with |O| >= 2 may exceed 1e-2
@@ -87,3 +91,33 @@ def assert_f32_parity(o, lse, ro, rl, what=""):
     assert st["max_o"] <= F32_MAX_ABS_O, msg
     assert st["max_lse"] <= F32_MAX_ABS_LSE, msg
     return st
+
+
+def assert_config_parity(o, lse, ro, rl, what="", fp32=False):
+    """The plain limits for the five benchmark configurations, with no
+    rounding allowance: bf16 max|dO| <= 1e-2, mean|dO| <= 1e-3,
+    max|dLSE| <= 1e-3 (and the internal relative-L2 gate); fp32
+    max|dO| <= 1e-5 and max|dLSE| <= 1e-5. Every output must be finite where
+    the oracle's is (outputs are filled with NaN before the call, so an
+    element no work item wrote fails here), and LSE is -inf exactly where the
+    oracle's is."""
+    assert np.array_equal(np.isneginf(lse), np.isneginf(rl)), f"{what}: -inf LSE pattern differs"
+    assert np.all(np.isfinite(o)), f"{what}: {int((~np.isfinite(o)).sum())} outputs not finite (unwritten?)"
+    assert np.all(np.isfinite(lse) | np.isneginf(rl)), f"{what}: LSE not finite"
+    st = parity_stats(o, lse, ro, rl)
+    msg = f"{what}: {st}"
+    if fp32:
+        assert st["max_o"] <= F32_MAX_ABS_O, msg
+        assert st["max_lse"] <= F32_MAX_ABS_LSE, msg
+    else:
+        assert st["max_o"] <= BF16_MAX_ABS_O, msg
+        assert st["mean_o"] <= BF16_MEAN_ABS_O, msg
+        assert st["max_lse"] <= BF16_MAX_ABS_LSE, msg
+        assert st["rel_l2"] <= BF16_REL_L2_O, msg
+    return st
+
+
+def nan_like(shape, dtype, dev):
+    """A device buffer filled with NaN, for outputs a kernel must overwrite."""
+    import torch
+    return torch.full(shape, float("nan"), dtype=dtype, device=dev)

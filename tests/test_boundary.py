@@ -167,3 +167,25 @@ def test_binding_rejects_host_tensors(lib_path):
     x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         ta.attn_fwd(x, x, x)
+
+
+def test_binding_rejects_wrong_output_shapes_before_any_launch(lib_path):
+    # an undersized out or lse would let the kernels write past the buffer:
+    # the binding refuses it before it looks at devices or calls the library
+    import torch
+    import tiled_attention_12_amd as ta
+    B, H, N = 2, 128, 10
+    bf = torch.bfloat16
+    q, qpe = torch.zeros(B, H, 512, dtype=bf), torch.zeros(B, H, 64, dtype=bf)
+    kv, kpe = torch.zeros(N, 512, dtype=bf), torch.zeros(N, 64, dtype=bf)
+    ind = torch.tensor([0, 4, N], dtype=torch.int32)
+    for out, lse in ((torch.zeros(B, H - 1, 512, dtype=bf), None),
+                     (torch.zeros(B, H, 256, dtype=bf), None),
+                     (None, torch.zeros(B, H - 1)),
+                     (None, torch.zeros(B * H))):
+        with pytest.raises(ValueError, match="out must be"):
+            ta.mla_decode(q, qpe, kv, kpe, ind, 0.05, out=out, lse=lse)
+    x = torch.zeros(1, 2, 8, 64, dtype=bf)
+    for out, lse in ((torch.zeros(1, 2, 7, 64, dtype=bf), None), (None, torch.zeros(1, 2, 7))):
+        with pytest.raises(ValueError):
+            ta.attn_fwd(x, x, x, out=out, lse=lse)

@@ -1,10 +1,12 @@
 """GPU parity of ssd_scan (the Mamba-2 state-space scan) against the CPU
 float64 oracle (needs gfx950).
 
-Element by element at sizes the oracle finishes quickly (several 64-step
+Element by element against the step-by-step definition
+(``oracle.ssd.ssd_recurrence``) at sizes it finishes quickly (several 64-step
 chunks and ragged tails, both workgroup shapes: two heads per workgroup when
 heads per group is even, one when it is odd), with and without initial and
-final states; on sampled heads at the full benchmark workload.
+final states; on sampled whole heads, again by the recurrence, at the full
+benchmark workload.
 
 Tolerance. The kernel rounds to bf16 at four points, as the reference
 Mamba-2 kernels do: the decay-weighted scores G inside a chunk, the
@@ -49,6 +51,22 @@ def _ref_inputs(d):
             inputs.stored_values(d["C"]))
 
 
+def _recurrence_heads(d, pairs):
+    """(y [n, L, P], final state [n, P, N]) of the selected (batch, head)
+    pairs by the step-by-step recurrence, one head at a time."""
+    x, dt, A, B, C = _ref_inputs(d)
+    H, G = x.shape[2], B.shape[2]
+    ys, fs = [], []
+    for b, h in pairs:
+        g = h // (H // G)
+        s0 = d["init_state"][b:b + 1, h:h + 1] if "init_state" in d else None
+        y, f = ossd.ssd_recurrence(x[b:b + 1, :, h:h + 1], dt[b:b + 1, :, h:h + 1], A[h:h + 1],
+                                   B[b:b + 1, :, g:g + 1], C[b:b + 1, :, g:g + 1], s0)
+        ys.append(y[0, :, 0])
+        fs.append(f[0, 0])
+    return np.stack(ys), np.stack(fs)
+
+
 def _run(ta, dev, d, final=False):
     x, B, C = (to_dev(d[n], dev) for n in ("x", "B", "C"))
     dt, A = to_dev(d["dt"], dev), to_dev(d["A"], dev)
@@ -90,7 +108,7 @@ def test_ssd_against_oracle(ta, dev, Bt, L, H, G, init, final):
     d = inputs.ssd_inputs(Bt, L, H, G, 64, 128, seed=7000 + L + H, init_state=init)
     print(f"ssd Bt={Bt} L={L} H={H} G={G} init={init} final={final}", flush=True)
     y, f = _run(ta, dev, d, final)
-    ry, rf = ossd.ssd_chunked(*_ref_inputs(d), 64, d.get("init_state"))
+    ry, rf = ossd.ssd_recurrence(*_ref_inputs(d), d.get("init_state"))
     _check(y.transpose(0, 2, 1, 3), ry.transpose(0, 2, 1, 3), "y", (2, 3))
     if final:
         _check(f, rf, "final state", (2, 3))
@@ -116,7 +134,7 @@ def test_ssd_extreme_decay_rates(ta, dev):
     d["A"][:2] = -16.0
     d["A"][2:] = -1.0
     y, f = _run(ta, dev, d, final=True)
-    ry, rf = ossd.ssd_chunked(*_ref_inputs(d), 64, d["init_state"])
+    ry, rf = ossd.ssd_recurrence(*_ref_inputs(d), d["init_state"])
     _check(y.transpose(0, 2, 1, 3), ry.transpose(0, 2, 1, 3), "y", (2, 3))
     _check(f, rf, "final state", (2, 3))
 
@@ -129,7 +147,7 @@ def test_ssd_full_workload_sampled_heads(ta, dev):
     rng = np.random.default_rng(5)
     pairs = [(0, 0), (w["Bt"] - 1, w["H"] - 1)] + [(int(rng.integers(w["Bt"])), int(rng.integers(w["H"])))
                                                     for _ in range(6)]
-    ry, rf = ossd.ssd_rows(*_ref_inputs(d), pairs, 64)
+    ry, rf = _recurrence_heads(d, pairs)
     for i, (b, h) in enumerate(pairs):
         _check(y[b, :, h][None], ry[i][None], f"y b={b} h={h}", (1, 2))
         _check(f[b, h][None], rf[i][None], f"final state b={b} h={h}", (1, 2))
@@ -140,7 +158,7 @@ def test_ssd_more_heads_than_one_pass_of_the_chip(ta, dev):
     d = inputs.ssd_inputs(16, 256, 80, 1, 64, 128, seed=7300)
     y, _ = _run(ta, dev, d)
     pairs = [(0, 0), (15, 79), (7, 40), (3, 1), (12, 63)]
-    ry, _ = ossd.ssd_rows(*_ref_inputs(d), pairs, 64)
+    ry, _ = _recurrence_heads(d, pairs)
     for i, (b, h) in enumerate(pairs):
         _check(y[b, :, h][None], ry[i][None], f"y b={b} h={h}", (1, 2))
 

@@ -1,7 +1,8 @@
 """Pins of the oracle's attention variants (grouped/single KV heads, sliding
 window, block mask), on the CPU.
 
-The variants are those of "TileLang study notes", section 5.1. Each test ties
+The variants are those of "TileLang programming model and FlashMLA",
+section 5.1. Each test ties
 ``oracle.attention_masked`` to something other than itself: closed forms on
 identical keys, the plain ``oracle.attention`` (itself pinned against a
 50-digit brute force and torch's float64 attention), and the exact

@@ -173,6 +173,10 @@ def mla_decode(q, q_pe, kv, k_pe, kv_indptr, scale, out=None, lse=None, stream=N
     N = kv.shape[0]
     if Dl != 512 or tuple(q_pe.shape) != (B, H, 64) or kv.shape[1] != 512 or tuple(k_pe.shape) != (N, 64):
         raise ValueError("MLA widths must be 512 (latent) and 64 (rotary)")
+    # the kernels write B*H rows of O and LSE: wrong-shaped buffers are
+    # rejected before any device check or launch
+    if (out is not None and tuple(out.shape) != (B, H, 512)) or (lse is not None and tuple(lse.shape) != (B, H)):
+        raise ValueError("out must be [B, H, 512] and lse [B, H]")
     dev = q.device
     for n, t in (("q", q), ("q_pe", q_pe), ("kv", kv), ("k_pe", k_pe)):
         _check_dev(n, t, torch.bfloat16, dev)
