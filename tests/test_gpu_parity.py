@@ -332,3 +332,51 @@ def test_more_items_than_compute_units_without_xcd_order(ta, dev, causal):
         sl = lambda n: inputs.stored_values(x[n][:, h:h + 1])
         ro, rl = oracle.attention(sl("q"), sl("k"), sl("v"), 0.088, causal=causal, rows=rows)
         assert_bf16_parity(o[:, h:h + 1, rows], lse[:, h:h + 1, rows], ro, rl, f"H=5 S={S} causal={causal} h={h}")
+
+
+# ------------------------------------------------------------------ running-max raises
+
+def test_bf16_running_max_rises_across_tiles(ta, dev):
+    # one query/key dimension carries a score ramp along the key index (about
+    # 9 base-2 units per 64 keys), so the running max is raised again and
+    # again after the first tile and the accumulator rescale runs; a rescale
+    # left out or applied twice would weight early keys by a factor 2^9 off
+    B, H, S, D = 1, 2, 1000, 128
+    x = inputs.mha_inputs(B, H, S, S, D, seed=41)
+    q = inputs.stored_values(x["q"]).copy()
+    k = inputs.stored_values(x["k"]).copy()
+    scale = float(np.float32(D ** -0.5))
+    q[..., 0] = 1.0
+    ramp = (9.0 / 64.0) * np.log(2.0) / scale  # natural-log score units per key
+    k[..., 0] = (ramp * np.arange(S, dtype=np.float64)).astype(np.float32)
+    y = dict(x, q=inputs.f32_to_bf16_bits(q), k=inputs.f32_to_bf16_bits(k))
+    for causal in (False, True):
+        o, lse = _run_mha(ta, dev, y, causal, scale)
+        ro, rl = oracle.attention(*_vals(y, "qkv"), scale, causal=causal)
+        assert_bf16_parity(o, lse, ro, rl, f"score ramp causal={causal}")
+
+
+@pytest.mark.parametrize("H", [32, 64, 128])
+def test_mla_running_max_rises_across_tiles(ta, dev, H):
+    # the rotary part carries a score ramp along each batch's keys (about 9
+    # base-2 units per 128 keys) and is not part of the values, so O stays
+    # small while the running max of every head rises tile after tile inside
+    # the pieces (16384 keys per batch: several tiles per piece)
+    lens = [16384, 16384, 9000, 16384]
+    B = len(lens)
+    m = inputs.mla_inputs(B, H, seed=42 + H, kv_len=1)
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n = int(indptr[-1])
+    g = np.random.default_rng(43 + H)
+    m["kv"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 512), dtype=np.float32) * np.float32(0.3))
+    scale = float(np.float32(576 ** -0.5))
+    u = np.full(64, 0.5, dtype=np.float32)
+    qpe = np.broadcast_to(u, (B, H, 64)) + g.standard_normal((B, H, 64), dtype=np.float32) * np.float32(0.01)
+    m["q_pe"] = inputs.f32_to_bf16_bits(qpe.astype(np.float32))
+    per_key = (9.0 / 128.0) * np.log(2.0) / (scale * float(u @ u))
+    pos = np.concatenate([np.arange(L) for L in lens]).astype(np.float64)
+    m["k_pe"] = inputs.f32_to_bf16_bits((per_key * pos)[:, None].astype(np.float32) * u[None, :])
+    m["indptr"] = indptr
+    o, lse = _run_mla(ta, dev, m, scale)
+    ro, rl = oracle.mla_decode(*_mla_vals(m), indptr, scale)
+    assert_bf16_parity(o, lse, ro, rl, f"mla score ramp H={H}")

@@ -26,14 +26,19 @@
 //  hardware hands workgroup i to XCD i % 8): the pieces of one batch then
 //  share that XCD's L2 for Q.
 //
-// gfx950 mapping of the split kernel: 4 waves x 32 heads (H = 128); wave w
-// holds Q^T of its heads in registers (B operand, 36 k-steps of 16) and the
-// O^T accumulator (16 blocks of 32 latent columns) in accumulation
-// registers. Per 32-key tile: S^T = KV * Q^T + K_pe * Q_pe^T with the tile
-// read from LDS as the A operand (v_mfma_f32_32x32x16_bf16), then the
-// online softmax in lane-per-head form, then O^T += KV^T * P^T with KV^T read
-// by ds_read_b64_tr_b16 from the same tile. Tiles arrive by
-// global_load_lds_dwordx4 through a 4-stage LDS ring.
+// gfx950 mapping of the split kernel: 4 waves x 32 heads (H = 128), one wave
+// per SIMD; wave w holds Q^T of its heads in registers (B operand, 36
+// k-steps of 16) and the O^T accumulator (16 blocks of 32 latent columns) in
+// the accumulation registers, which it fills. Per 32-key tile:
+// S^T = KV * Q^T + K_pe * Q_pe^T with the tile read from LDS as the A operand
+// (v_mfma_f32_32x32x16_bf16, the score accumulator pinned to ordinary
+// VGPRs), the online softmax in lane-per-head form, and O^T += KV^T * P^T
+// with KV^T read by ds_read_b64_tr_b16 from the same tile. The tile loop is
+// software pipelined: step i scores tile i and runs its softmax, then
+// accumulates P*V of tile i-1. Tiles arrive by global_load_lds_dwordx4
+// through a 4-stage LDS ring with two tiles in flight; latent rows are
+// padded in LDS so both read patterns are conflict-free with one base
+// register each.
 #include "device_common.h"
 #include "launch.h"
 
@@ -42,7 +47,8 @@ namespace tattn {
 constexpr int kDl = 512;     // latent width
 constexpr int kDr = 64;      // rotary width
 constexpr int kBK = 32;      // keys per tile
-constexpr int kTileL = kBK * kDl * 2;
+constexpr int kRowL = kDl * 2 + 48;   // latent row stride in LDS (1 KB + 48 B of padding)
+constexpr int kTileL = kBK * kRowL;
 constexpr int kTileR = kBK * kDr * 2;
 constexpr int kStage = kTileL + kTileR;
 // Up to this many batches the split kernel forms the tile prefix itself (in
@@ -201,6 +207,24 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a, int P) {
   if ((threadIdx.x & 31) == 0) a.lse[(size_t)b * H + h] = tot > 0.f ? mx + __logf(tot) : -INFINITY;
 }
 
+// S += A * B on v_mfma_f32_32x32x16_bf16 with the accumulator pinned to
+// VGPRs (inline asm): the score tile then never competes with O for the
+// accumulation registers, which O fills, and no accumulator is moved
+// between the two register files inside the tile loop. LAST appends the
+// wait states a VALU access to the result needs after the final MFMA of a
+// chain (the compiler does not see this MFMA).
+template <bool FIRST, bool LAST>
+__device__ __forceinline__ void mfma32_v(f32x16& s, bf16x8 a, bf16x8 b) {
+  if constexpr (FIRST && LAST)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4" : "=v"(s) : "v"(a), "v"(b));
+  else if constexpr (FIRST)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(a), "v"(b));
+  else if constexpr (LAST)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 4" : "+v"(s) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(a), "v"(b));
+}
+
 template <int NW, int NSTAGE, bool FUSE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_split_kernel(MlaArgs a) {
@@ -210,8 +234,10 @@ void mla_split_kernel(MlaArgs a) {
   constexpr int LAT_LOADS = kBK / NW;           // one 1 KB latent row per wave load
   constexpr int PE_LOADS = kBK * (kDr / 8) / (64 * NW);
   constexpr int LPT = LAT_LOADS + PE_LOADS;     // loads per wave per tile
+  constexpr int PF = NSTAGE - 2;                // tiles in flight ahead of the scored one
   static_assert(kBK * (kDr / 8) % (64 * NW) == 0, "rotary tile must split into wave loads");
-  static_assert((NSTAGE - 2) * LPT < 64, "vmcnt range");
+  static_assert(PF * LPT < 64, "vmcnt range");
+  static_assert(PF == 1 || PF == 2, "ring of 3 or 4 stages");
   constexpr float TAU = 8.0f;
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -222,33 +248,27 @@ void mla_split_kernel(MlaArgs a) {
   const int H = a.H;
   const int head = wave * 32 + col;
   const float c = a.c;
+  const uint32_t smem0 = lds_addr(smem);
 
-  // Lane-dependent parts of the LDS addresses. The swizzle only permutes the
-  // low 4 chunk bits, so every read is one of these bases plus a constant
-  // (higher chunk bits, row half, stage) that fits the instruction offset.
-  uint32_t kbase[8], pbase[4], tbase[2][4];
-  {
-    const int sg = ((col & 3) << 2) | ((col >> 2) & 3);
+  // Lane-dependent LDS offsets inside a stage. Latent rows are padded to
+  // kRowL bytes, so each latent read is one base register plus an
+  // instruction offset: the score operand (key row col, 16-byte chunk
+  // 2*ks + hi; 16 consecutive rows at one chunk hit 16 distinct 4-bank
+  // groups) and the transposing reads of the value operand (a 16-lane group
+  // reads 32 bytes from each of four consecutive key rows, 48 bytes of bank
+  // offset apart). The rotary rows keep the XOR swizzle of their loads.
+  const uint32_t kb_off = (uint32_t)(col * kRowL + 16 * hi);
+  uint32_t pb_off[4];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) kbase[r] = col * 1024 + 16 * ((2 * r + hi) ^ sg);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pbase[r] = kTileL + col * 128 + 16 * swz<8>(col, 2 * r + hi);
-    const int gq = (lane >> 4) & 1, s16 = lane & 15;
-    const int x = 2 * gq + ((s16 & 3) >> 1), boff = 8 * (s16 & 1);
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int rr = 8 * e + 4 * hi + (s16 >> 2);
-      const int sr = ((rr & 3) << 2) | ((rr >> 2) & 3);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) tbase[e][r] = rr * 1024 + 16 * ((4 * r + x) ^ sr) + boff;
-    }
-  }
+  for (int r = 0; r < 4; ++r) pb_off[r] = kTileL + col * 128 + 16 * swz<8>(col, 2 * r + hi);
+  const uint32_t tb_off =
+      (uint32_t)((4 * hi + ((lane & 15) >> 2)) * kRowL + 32 * ((lane >> 4) & 1) + 8 * (lane & 3));
 
-  // Tile prefix: tile_ptr[b] = tiles of batches before b. With fuse_plan the
+  // Tile prefix: tile_ptr[b] = tiles of batches before b. With FUSE the
   // workgroup forms it in LDS (and workgroup 0 also writes it out for the
   // merge kernel); otherwise the plan kernel has written it.
   typedef __attribute__((address_space(3))) int lds_int;
-  lds_int* tp_lds = (lds_int*)(uintptr_t)lds_addr(smem + NSTAGE * kStage);
+  lds_int* tp_lds = (lds_int*)(uintptr_t)(smem0 + NSTAGE * kStage);
   if constexpr (FUSE) {
     const int B = a.B, nthr = NW * 64, t = threadIdx.x;
     const int per = (B + nthr - 1) / nthr;
@@ -307,9 +327,10 @@ void mla_split_kernel(MlaArgs a) {
     wait_lgkmcnt0();
     barrier();
 
-    // Tile i of this piece -> LDS stage i % NSTAGE. Every latent load of a
-    // wave covers one key row (uniform, so its base address is scalar); the
-    // lane picks the global chunk lane ^ sigma(row). Rotary loads cover 8 rows.
+    // Tile i of this piece -> LDS stage i % NSTAGE. A latent load of a wave
+    // covers one whole key row (rows past the batch repeat its last row, so
+    // the prologue may load tiles past the piece's end); rotary loads cover
+    // 8 rows with the chunk order swizzled on the global side.
     auto issue = [&](int i) {
       char* sl = smem + (i % NSTAGE) * kStage;
       const int key0 = kv_lo + (t0 + i) * kBK;
@@ -317,22 +338,22 @@ void mla_split_kernel(MlaArgs a) {
       for (int n = 0; n < LAT_LOADS; ++n) {
         const int row = n * NW + wave;
         const int gr = min(key0 + row, kv_hi - 1);
-        const char* rowp = (const char*)(a.kv + (size_t)gr * kDl);
-        const uint32_t voff = (uint32_t)swz<64>(row, lane) * 16u;
-        load_lds16(rowp + voff, sl + row * 1024);
+        load_lds16((const char*)(a.kv + (size_t)gr * kDl) + 16 * lane, sl + row * kRowL);
       }
 #pragma unroll
       for (int n = 0; n < PE_LOADS; ++n) {
         const int slot = (n * NW + wave) * 64 + lane;
         const int row = slot >> 3;
-        const int rc = min(row, kv_hi - 1 - key0);
-        const char* tilep = (const char*)(a.kpe + (size_t)key0 * kDr);
-        const uint32_t voff = (uint32_t)(rc * kDr * 2 + swz<8>(row, slot & 7) * 16);
-        load_lds16(tilep + voff, sl + kTileL + (n * NW + wave) * 1024);
+        const int gr = min(key0 + row, kv_hi - 1);
+        load_lds16((const char*)(a.kpe + (size_t)gr * kDr) + swz<8>(row, slot & 7) * 16,
+                   sl + kTileL + (n * NW + wave) * 1024);
       }
     };
+#pragma unroll
+    for (int i = 0; i < PF; ++i) issue(i);
 
-    // Q^T fragments of this wave's heads
+    // Q^T fragments of this wave's heads (after the first tiles' loads, so
+    // they travel together)
     bf16x8 qf[KS];
     {
       const uint16_t* qr = a.q + ((size_t)b * H + head) * kDl + hi * 8;
@@ -343,118 +364,142 @@ void mla_split_kernel(MlaArgs a) {
       for (int ks = KSL; ks < KS; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(pr + (ks - KSL) * 16));
     }
 
-#pragma unroll
-    for (int i = 0; i < NSTAGE - 1; ++i)
-      if (i < nt) issue(i);
-
     f32x16 oacc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) oacc[db] = f32x16{};
     float m = -INFINITY, lsum = 0.f;
 
-    for (int i = 0; i < nt; ++i) {
-      const int ahead = min(NSTAGE - 2, nt - 1 - i);
-      if constexpr (NSTAGE == 4) {
-        if (ahead >= 2) wait_vmcnt<2 * LPT>();
-        else if (ahead == 1) wait_vmcnt<LPT>();
-        else wait_vmcnt<0>();
-      } else {
-        if (ahead >= 1) wait_vmcnt<LPT>();
-        else wait_vmcnt<0>();
+    // ---- S^T = KV * Q^T + K_pe * Q_pe^T of the tile in stage st, the
+    // operand reads six k-steps ahead of their MFMAs
+    auto score = [&](int st, f32x16& s) {
+      const uint32_t kb = smem0 + (uint32_t)(st * kStage) + kb_off;
+      const uint32_t pb = smem0 + (uint32_t)(st * kStage);
+      constexpr int AHEAD = 6;
+      auto kread = [&](auto KSc) -> u32x4 {
+        constexpr int ks = decltype(KSc)::value;
+        if constexpr (ks < KSL) return lds_read128_async<32 * ks>(kb);
+        else return lds_read128_async<0>(pb + pb_off[ks - KSL]);
+      };
+      u32x4 kr[AHEAD];
+      static_for<AHEAD>([&](auto KSc) { kr[decltype(KSc)::value] = kread(KSc); });
+      static_for<KS>([&](auto KSc) {
+        constexpr int ks = decltype(KSc)::value, slot = ks % AHEAD;
+        constexpr int later = (KS - 1 - ks) < (AHEAD - 1) ? (KS - 1 - ks) : (AHEAD - 1);
+        wait_lds_tied_n4<later>(kr[slot]);
+        mfma32_v<ks == 0, ks == KS - 1>(s, as_bf16x8(kr[slot]), qf[ks]);
+        if constexpr (ks + AHEAD < KS) kr[slot] = kread(std::integral_constant<int, ks + AHEAD>{});
+      });
+    };
+    // ---- online softmax (lane = head): the running max is raised only past
+    // the threshold (then alpha < 1 rescales l here and O by the caller),
+    // P^T in bf16, row sums from the unrounded P
+    auto softmax = [&](const f32x16& s, bf16x8 (&pf)[2], bool& raised, float& alpha) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, s[i2]);
+      mx = max_halves(mx) * c;
+      raised = mx - m > TAU;  // false when mx == -inf
+      alpha = raised ? fast_exp2(m - mx) : 1.f;
+      m = raised ? mx : m;
+      lsum *= alpha;
+      const float mc = m == -INFINITY ? 0.f : m;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float p[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          p[j] = fast_exp2(fmaf(s[half * 8 + j], c, -mc));
+          lsum += p[j];
+        }
+        u32x4 x = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                   pack_bf16x2(p[6], p[7])};
+        pf[half] = as_bf16x8(x);
       }
-      barrier();
-      if (i + NSTAGE - 1 < nt) issue(i + NSTAGE - 1);
-
-      const char* sl = smem + (i % NSTAGE) * kStage;
+    };
+    // ---- O^T += KV^T * P^T for the tile in stage st (KV^T by transposing
+    // reads of the same latent rows), half 0 of every d-block, then half 1;
+    // the reads of four steps are in flight
+    auto pv = [&](int st, const bf16x8 (&pf)[2]) {
+      const uint32_t vb = smem0 + (uint32_t)(st * kStage) + tb_off;
+      constexpr int NSTEP = 2 * DB;
+      constexpr int AHEAD = 4;
+      auto vread = [&](auto SC, u32x2 (&r)[2]) {
+        constexpr int stp = decltype(SC)::value, half = stp / DB, db = stp % DB;
+        constexpr int off = half * 16 * kRowL + db * 64;
+        r[0] = lds_read_tr16_async<off>(vb);
+        r[1] = lds_read_tr16_async<off + 8 * kRowL>(vb);
+      };
+      u32x2 vr[AHEAD][2];
+      static_for<AHEAD>([&](auto SC) { vread(SC, vr[decltype(SC)::value]); });
+      static_for<NSTEP>([&](auto SC) {
+        constexpr int stp = decltype(SC)::value, half = stp / DB, db = stp % DB;
+        constexpr int slot = stp % AHEAD;
+        constexpr int later = (NSTEP - 1 - stp) < (AHEAD - 1) ? (NSTEP - 1 - stp) : (AHEAD - 1);
+        wait_lds_tied_n<2 * later>(vr[slot][0], vr[slot][1]);
+        oacc[db] = mfma32(cat_tr(vr[slot][0], vr[slot][1]), pf[half], oacc[db]);
+        if constexpr (stp + AHEAD < NSTEP) vread(std::integral_constant<int, stp + AHEAD>{}, vr[slot]);
+      });
+    };
+    // ---- the rare O rescale after a raise, in place in the accumulation
+    // registers (wait states first: the last P*V MFMA wrote them)
+    auto rescale = [&](bool raised, float alpha) {
+      if (__builtin_amdgcn_ballot_w64(raised)) {
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 4" ::: "memory");
+        static_for<DB>([&](auto DBc) { scale_acc16(oacc[DBc], alpha); });
+      }
+    };
+    // the piece's last tile may be partial: keys past the batch score -inf
+    auto tail_mask = [&](int i, f32x16& s) {
       const int nvalid = min(kBK, kv_hi - (kv_lo + (t0 + i) * kBK));
-
-      // ---- S^T = KV * Q^T + K_pe * Q_pe^T
-      const uint32_t sbase = lds_addr(sl);
-      f32x16 s = f32x16{};
-      {
-        // operand reads run AHEAD k-steps in front of their MFMAs
-        constexpr int AHEAD = 6;
-        auto kread = [&](auto KSc) -> u32x4 {
-          constexpr int ks = decltype(KSc)::value;
-          if constexpr (ks < KSL) return lds_read128_async<256 * (ks >> 3)>(sbase + kbase[ks & 7]);
-          else return lds_read128_async<0>(sbase + pbase[ks - KSL]);
-        };
-        u32x4 kr[AHEAD];
-        static_for<AHEAD>([&](auto KSc) { kr[decltype(KSc)::value] = kread(KSc); });
-        static_for<KS>([&](auto KSc) {
-          constexpr int ks = decltype(KSc)::value, slot = ks % AHEAD;
-          constexpr int later = (KS - 1 - ks) < (AHEAD - 1) ? (KS - 1 - ks) : (AHEAD - 1);
-          wait_lds_tied_n4<later>(kr[slot]);
-          s = mfma32(as_bf16x8(kr[slot]), qf[ks], s);
-          if constexpr (ks + AHEAD < KS) kr[slot] = kread(std::integral_constant<int, ks + AHEAD>{});
-        });
-      }
-
       if (nvalid < kBK) {
 #pragma unroll
         for (int i2 = 0; i2 < 16; ++i2)
           if (8 * (i2 >> 2) + 4 * hi + (i2 & 3) >= nvalid) s[i2] = -INFINITY;
       }
+    };
+    // tile i in LDS, every wave past P*V of tile i-2 (so the refill of
+    // tile i+PF may overwrite its stage), then that refill issued
+    auto wait_tile = [&](int i) {
+      // the tiles issued before step i are 0 .. max(PF-1, min(i+PF-1, nt-1))
+      const int last = max(PF - 1, min(i + PF - 1, nt - 1));
+      if (last > i) wait_vmcnt<LPT>();
+      else wait_vmcnt<0>();
+      barrier();
+      if (i + PF < nt) issue(i + PF);
+    };
 
-      // ---- online softmax (lane = head)
-      bf16x8 pf[2];
-      {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int i2 = 0; i2 < 16; ++i2) mx = fmaxf(mx, s[i2]);
-        mx = max_halves(mx) * c;
-        const bool raise = mx - m > TAU;
-        if (__builtin_amdgcn_ballot_w64(raise)) {
-          const float alpha = raise ? fast_exp2(m - mx) : 1.f;
-          m = raise ? mx : m;
-          lsum *= alpha;
-          static_for<DB>([&](auto DBc) { scale_acc16(oacc[DBc], alpha); });
-        }
-        const float mc = m == -INFINITY ? 0.f : m;
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          float p[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(fmaf(s[half * 8 + j], c, -mc));
-            lsum += p[j];
-          }
-          u32x4 x = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                     pack_bf16x2(p[6], p[7])};
-          pf[half] = as_bf16x8(x);
-        }
-      }
-
-      // ---- O^T += KV^T * P^T (KV^T by transposing reads of the latent tile):
-      // half 0 of every d-block, then half 1, so consecutive MFMAs use
-      // different accumulators; the reads of the next step are in flight
-      // while the current MFMA runs.
-      {
-        uint32_t vb[2][4];
-#pragma unroll
-        for (int e = 0; e < 2; ++e)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) vb[e][r] = sbase + tbase[e][r];
-        constexpr int NSTEP = 2 * DB;
-        constexpr int AHEAD = 4;  // steps whose reads are in flight
-        auto vread = [&](auto SC, u32x2 (&r)[2]) {
-          constexpr int stp = decltype(SC)::value, half = stp / DB, db = stp % DB;
-          r[0] = lds_read_tr16_async<half * 16384 + (db >> 2) * 256>(vb[0][db & 3]);
-          r[1] = lds_read_tr16_async<half * 16384 + (db >> 2) * 256>(vb[1][db & 3]);
-        };
-        u32x2 vr[AHEAD][2];
-        static_for<AHEAD>([&](auto SC) { vread(SC, vr[decltype(SC)::value]); });
-        static_for<NSTEP>([&](auto SC) {
-          constexpr int stp = decltype(SC)::value, half = stp / DB, db = stp % DB;
-          constexpr int slot = stp % AHEAD;
-          // reads of the later in-flight steps may still be outstanding
-          constexpr int later = (NSTEP - 1 - stp) < (AHEAD - 1) ? (NSTEP - 1 - stp) : (AHEAD - 1);
-          wait_lds_tied_n<2 * later>(vr[slot][0], vr[slot][1]);
-          oacc[db] = mfma32(cat_tr(vr[slot][0], vr[slot][1]), pf[half], oacc[db]);
-          if constexpr (stp + AHEAD < NSTEP) vread(std::integral_constant<int, stp + AHEAD>{}, vr[slot]);
-        });
-      }
+    // Software pipeline over the piece's tiles: step i scores tile i, runs
+    // its softmax and then accumulates P*V of tile i-1 (whose P the previous
+    // step produced), so the MFMAs of one tile's product follow the VALU
+    // work of the other's without waiting for it. O is rescaled after P*V
+    // of tile i-1 when tile i raised the running max.
+    bf16x8 pf_prev[2];
+    {
+      wait_tile(0);
+      f32x16 s;
+      score(0, s);
+      if (nt == 1) tail_mask(0, s);
+      bool raised;
+      float alpha;
+      softmax(s, pf_prev, raised, alpha);  // O is still zero: nothing to rescale
     }
+    auto step = [&](int i, auto LASTc) {
+      wait_tile(i);
+      f32x16 s;
+      score(i % NSTAGE, s);
+      if constexpr (decltype(LASTc)::value) tail_mask(i, s);
+      bf16x8 pf[2];
+      bool raised;
+      float alpha;
+      softmax(s, pf, raised, alpha);
+      pv((i - 1) % NSTAGE, pf_prev);
+      rescale(raised, alpha);
+      pf_prev[0] = pf[0];
+      pf_prev[1] = pf[1];
+    };
+    for (int i = 1; i + 1 < nt; ++i) step(i, std::false_type{});
+    if (nt > 1) step(nt - 1, std::true_type{});
+    pv((nt - 1) % NSTAGE, pf_prev);
 
     // ---- normalised partial of this piece -> slot (workgroup + batch). The
     // rows go through LDS (the ring is free once every wave has passed the
@@ -467,7 +512,8 @@ void mla_split_kernel(MlaArgs a) {
       static_assert(NW * 32 * SRS <= NSTAGE * kStage, "staging fits the ring");
       typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
       typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-      const uint32_t stg = lds_addr(smem) + wave * 32 * SRS;
+      const uint32_t stg = smem0 + wave * 32 * SRS;
+      wait_vmcnt<0>();  // the prologue may have loaded tiles past the piece's end
       barrier();
 #pragma unroll
       for (int db = 0; db < DB; ++db)
