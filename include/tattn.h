@@ -46,6 +46,7 @@ extern "C" {
 #define TATTN_ERR_ALIGN       (-3) /* a pointer misses its required alignment           */
 #define TATTN_ERR_OOM         (-4) /* device workspace could not be allocated           */
 #define TATTN_ERR_HIP         (-5) /* no usable HIP device, or a launch failed           */
+#define TATTN_ERR_SCRATCH     (-6) /* mla_decode_noalloc: workspace above its static cap */
 
 /*
  * attn_fwd -- multi-head attention forward, bf16 in, fp32 accumulate.
@@ -162,6 +163,27 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
 int mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe,
                void* o, float* lse, int B, int H, const int32_t* kv_indptr,
                float scale, void* stream);
+
+/*
+ * mla_decode_noalloc -- mla_decode for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, layouts, results and status codes as
+ * mla_decode (same kernels, bit-identical output); it allocates nothing,
+ * creates no event and only enqueues kernel launches on `stream`.
+ *
+ * Its workspace (the split plan and the per-piece partial outputs, the
+ * same (CUs + B) * H * (512 * 2 + 4) bytes plus the plan that mla_decode
+ * needs) is a static array of 64 MiB inside the library, one per GPU the
+ * library runs on, held until the process ends. A request whose workspace
+ * exceeds 64 MiB returns TATTN_ERR_SCRATCH before any launch (on a 256-CU
+ * MI355X at H = 128 that is more than about 250 batches). Every call on one
+ * GPU uses that GPU's array and leaves its contents behind: calls whose
+ * kernels overlap on one GPU (different streams without ordering between
+ * them) race and give wrong results; calls ordered on one stream are safe.
+ */
+int mla_decode_noalloc(const void* q, const void* q_pe, const void* kv, const void* k_pe,
+                       void* o, float* lse, int B, int H, const int32_t* kv_indptr,
+                       float scale, void* stream);
 
 /*
  * ssd_scan -- Mamba-2 state-space scan (chunk state, state passing and chunk

@@ -82,6 +82,15 @@ int main() {
          TATTN_OK);
   expect("mla valid, no device",
          mla_decode(P(16), P(16), P(16), P(16), P(16), F(16), 2, 128, I(16), 0.05f, nullptr), TATTN_ERR_HIP);
+  expect("mla noalloc H=96", mla_decode_noalloc(P(16), P(16), P(16), P(16), P(16), F(16), 2, 96, I(16), 0.05f,
+                                                 nullptr),
+         TATTN_ERR_UNSUPPORTED);
+  expect("mla noalloc null q", mla_decode_noalloc(nullptr, P(16), P(16), P(16), P(16), F(16), 2, 128, I(16),
+                                                   0.05f, nullptr),
+         TATTN_ERR_INVALID_ARG);
+  expect("mla noalloc valid, no device",
+         mla_decode_noalloc(P(16), P(16), P(16), P(16), P(16), F(16), 2, 128, I(16), 0.05f, nullptr),
+         TATTN_ERR_HIP);
   // ssd_scan
   expect("ssd G 3", ssd_scan(P(16), F(4), F(4), P(16), P(16), P(16), nullptr, nullptr, 2, 100, 8, 3, 64, 128,
                              nullptr),
@@ -93,7 +102,7 @@ int main() {
          ssd_scan(P(16), F(4), F(4), P(16), P(16), P(16), nullptr, nullptr, 1, 64, 2, 1, 64, 128, nullptr),
          TATTN_ERR_HIP);
   // status strings
-  for (int s = -6; s <= 1; ++s) {
+  for (int s = -7; s <= 1; ++s) {
     const char* t = tattn_status_str(s);
     if (!t || !std::strlen(t)) {
       std::fprintf(stderr, "FAIL status string %d\n", s);

@@ -34,6 +34,12 @@ hipError_t launch_mla_decode(const void*, const void*, const void*, const void*,
   return hipSuccess;
 }
 
+hipError_t mla_noalloc_scratch(void** ptr) {
+  static char host_stand_in[64];
+  *ptr = host_stand_in;
+  return hipSuccess;
+}
+
 hipError_t launch_ssd_scan_bf16(const void*, const float*, const float*, const void*, const void*, void*,
                                 const float*, float*, int, int, int, int, hipStream_t) {
   ++g_stub_launches;

@@ -20,8 +20,8 @@ def _header_symbols():
 
 
 def test_header_declares_the_entry_points():
-    assert _header_symbols() == ["attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "ssd_scan",
-                                 "tattn_status_str"]
+    assert _header_symbols() == ["attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "mla_decode_noalloc",
+                                 "ssd_scan", "tattn_status_str"]
 
 
 def test_library_exports_every_declared_symbol(lib_path):
@@ -41,7 +41,7 @@ def L(lib_path):
 
 
 F = ctypes.c_float
-OK, INVALID, UNSUP, ALIGN, OOM, HIP = 0, -1, -2, -3, -4, -5
+OK, INVALID, UNSUP, ALIGN, OOM, HIP, SCRATCH = 0, -1, -2, -3, -4, -5, -6
 
 
 def _mha(L, fn, q=16, k=16, v=16, o=16, lse=16, B=1, H=1, Sq=8, Skv=8, D=128, causal=0, scale=0.1):
@@ -92,9 +92,10 @@ def test_mha_ex_argument_validation(L):
     assert call(H=0, Hkv=0, q=None) == OK
 
 
-def test_mla_argument_validation(L):
+@pytest.mark.parametrize("fn", ["mla_decode", "mla_decode_noalloc"])
+def test_mla_argument_validation(L, fn):
     def call(q=16, qpe=16, kv=16, kpe=16, o=16, lse=16, B=2, H=128, ind=16, scale=0.05):
-        return L.mla_decode(q, qpe, kv, kpe, o, lse, B, H, ind, F(scale), None)
+        return getattr(L, fn)(q, qpe, kv, kpe, o, lse, B, H, ind, F(scale), None)
     assert call(q=None) == INVALID
     assert call(ind=None) == INVALID
     assert call(B=-1) == INVALID
@@ -142,22 +143,23 @@ def test_valid_request_without_gpu_is_a_hip_error(lib_path):
         "r3=L.mla_decode(16,16,16,16,16,16,2,128,16,F(0.1),None);"
         "r4=L.attn_fwd_ex(16,16,16,16,16,1,4,1,8,8,128,1,3,None,F(0.1),None);"
         "r5=L.ssd_scan(16,16,16,16,16,16,None,None,1,64,2,1,64,128,None);"
-        "print(r1,r2,r3,r4,r5)"
+        "r6=L.mla_decode_noalloc(16,16,16,16,16,16,2,128,16,F(0.1),None);"
+        "print(r1,r2,r3,r4,r5,r6)"
     )
     env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1", CUDA_VISIBLE_DEVICES="-1")
     out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, env=env, timeout=120)
     assert out.returncode == 0, out.stderr
-    assert out.stdout.split() == [str(HIP)] * 5
+    assert out.stdout.split() == [str(HIP)] * 6
 
 
 def test_status_strings_cover_every_code(L):
     from tiled_attention_12_amd import _binding
     seen = set()
-    for code in (OK, INVALID, UNSUP, ALIGN, OOM, HIP):
+    for code in (OK, INVALID, UNSUP, ALIGN, OOM, HIP, SCRATCH):
         s = _binding.status_str(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 6
+    assert len(seen) == 7
     assert _binding.status_str(7) == "unknown status"
 
 

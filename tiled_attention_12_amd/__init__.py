@@ -7,7 +7,8 @@ The binding is loaded on first attribute access, so ``inputs`` and
 entry point without the built library raises ImportError.
 """
 
-_EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "ssd_scan", "status_str", "TattnError", "lib")
+_EXPORTS = ("attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "mla_decode_noalloc", "ssd_scan", "status_str",
+            "TattnError", "lib")
 
 
 def __getattr__(name):

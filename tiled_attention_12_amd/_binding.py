@@ -18,8 +18,10 @@ TATTN_ERR_UNSUPPORTED = -2
 TATTN_ERR_ALIGN = -3
 TATTN_ERR_OOM = -4
 TATTN_ERR_HIP = -5
+TATTN_ERR_SCRATCH = -6
 
-EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "ssd_scan", "tattn_status_str")
+EXPORTED = ("attn_fwd", "attn_fwd_ex", "attn_fwd_f32", "mla_decode", "mla_decode_noalloc", "ssd_scan",
+            "tattn_status_str")
 
 
 class TattnError(RuntimeError):
@@ -43,8 +45,9 @@ def _load():
     lib.attn_fwd_f32.restype = i32
     lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, f32, vp]
     lib.attn_fwd_ex.restype = i32
-    lib.mla_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, f32, vp]
-    lib.mla_decode.restype = i32
+    for fn in (lib.mla_decode, lib.mla_decode_noalloc):
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, vp, f32, vp]
+        fn.restype = i32
     lib.ssd_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     lib.ssd_scan.restype = i32
     lib.tattn_status_str.argtypes = [i32]
@@ -163,9 +166,7 @@ def attn_fwd_f32(q, k, v, causal=False, scale=None, out=None, lse=None, stream=N
     return _mha("attn_fwd_f32", q, k, v, causal, scale, out, lse, stream, _torch().float32)
 
 
-def mla_decode(q, q_pe, kv, k_pe, kv_indptr, scale, out=None, lse=None, stream=None):
-    """MLA decode: q [B,H,512], q_pe [B,H,64], kv [N,512], k_pe [N,64] (bf16),
-    kv_indptr int32 [B+1] on the device. Returns (O bf16 [B,H,512], LSE fp32 [B,H])."""
+def _mla(fn_name, q, q_pe, kv, k_pe, kv_indptr, scale, out, lse, stream):
     torch = _torch()
     if q.dim() != 3 or q_pe.dim() != 3 or kv.dim() != 2 or k_pe.dim() != 2:
         raise ValueError("q [B,H,512], q_pe [B,H,64], kv [N,512], k_pe [N,64]")
@@ -189,11 +190,23 @@ def mla_decode(q, q_pe, kv, k_pe, kv_indptr, scale, out=None, lse=None, stream=N
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     _check_dev("out", out, torch.bfloat16, dev)
     _check_dev("lse", lse, torch.float32, dev)
-    rc = _LIB.mla_decode(_ptr(q), _ptr(q_pe), _ptr(kv), _ptr(k_pe), _ptr(out), _ptr(lse), B, H,
-                         _ptr(kv_indptr), ctypes.c_float(float(scale)), _stream_ptr(dev, stream))
+    rc = getattr(_LIB, fn_name)(_ptr(q), _ptr(q_pe), _ptr(kv), _ptr(k_pe), _ptr(out), _ptr(lse), B, H,
+                                _ptr(kv_indptr), ctypes.c_float(float(scale)), _stream_ptr(dev, stream))
     if rc != TATTN_OK:
-        raise TattnError(rc, "mla_decode")
+        raise TattnError(rc, fn_name)
     return out, lse
+
+
+def mla_decode(q, q_pe, kv, k_pe, kv_indptr, scale, out=None, lse=None, stream=None):
+    """MLA decode: q [B,H,512], q_pe [B,H,64], kv [N,512], k_pe [N,64] (bf16),
+    kv_indptr int32 [B+1] on the device. Returns (O bf16 [B,H,512], LSE fp32 [B,H])."""
+    return _mla("mla_decode", q, q_pe, kv, k_pe, kv_indptr, scale, out, lse, stream)
+
+
+def mla_decode_noalloc(q, q_pe, kv, k_pe, kv_indptr, scale, out=None, lse=None, stream=None):
+    """mla_decode with the library's static workspace (no device allocation by
+    the library; pass ``out`` and ``lse`` to keep torch from allocating too)."""
+    return _mla("mla_decode_noalloc", q, q_pe, kv, k_pe, kv_indptr, scale, out, lse, stream)
 
 
 def ssd_scan(x, dt, A, B, C, init_state=None, final_state=False, out=None, stream=None):

@@ -23,6 +23,11 @@ hipError_t launch_mha_fwd_f32(const float* q, const float* k, const float* v, fl
 // split over `n_split` workgroups.
 size_t mla_workspace_bytes(int B, int H, int n_split);
 
+// Size of the static workspace of mla_decode_noalloc, and its device
+// address on the current device (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+hipError_t mla_noalloc_scratch(void** ptr);
+
 hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe,
                              void* o, float* lse, int B, int H, const int32_t* kv_indptr,
                              float scale, int n_split, void* workspace, hipStream_t stream);

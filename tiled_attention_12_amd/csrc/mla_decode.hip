@@ -39,6 +39,8 @@
 // through a 4-stage LDS ring with two tiles in flight; latent rows are
 // padded in LDS so both read patterns are conflict-free with one base
 // register each.
+#include <mutex>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -593,6 +595,37 @@ hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, co
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3(B, (H + 7) / 8), dim3(256), 0, stream, a, n_split);
   return hipGetLastError();
+}
+
+// ---- static workspace of mla_decode_noalloc
+//
+// kNoAllocScratchBytes of device memory in the library's own code object,
+// one copy per GPU the library runs on, held until the process ends. In
+// host code `scratch` names a host-side stand-in, not the device array: its
+// device address comes from hipGetSymbolAddress, looked up once per device
+// with that device current and kept here; only that address is passed on.
+// Nothing in the workspace needs to start at zero (every slot the merge
+// reads was written by the same call), so the calls clear nothing.
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t mla_noalloc_scratch(void** ptr) {
+  constexpr int kMaxDevices = 256;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace tattn

@@ -126,21 +126,33 @@ TATTN_API int attn_fwd_f32(const float* q, const float* k, const float* v, float
                                              (hipStream_t)stream));
 }
 
-TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe, void* o, float* lse,
-                         int B, int H, const int32_t* kv_indptr, float scale, void* stream) {
+// Shared validation of the two MLA entry points. Returns TATTN_OK with
+// *nothing = true when there is no work.
+static int check_mla(const void* q, const void* q_pe, const void* kv, const void* k_pe, const void* o,
+                     const void* lse, int B, int H, const int32_t* kv_indptr, float scale, bool* nothing) {
+  *nothing = false;
   if (B < 0 || H < 0) return TATTN_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.f)) return TATTN_ERR_INVALID_ARG;
-  if (B == 0) return TATTN_OK;
+  if (B == 0) {
+    *nothing = true;
+    return TATTN_OK;
+  }
   if (H != 32 && H != 64 && H != 128) return TATTN_ERR_UNSUPPORTED;
   if (!q || !q_pe || !kv || !k_pe || !o || !lse || !kv_indptr) return TATTN_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(q_pe, 16) || !aligned(kv, 16) || !aligned(k_pe, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(kv_indptr, 4))
     return TATTN_ERR_ALIGN;
   if ((long long)B * H > INT_MAX || B > (1 << 24)) return TATTN_ERR_UNSUPPORTED;
+  return TATTN_OK;
+}
 
+TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe, void* o, float* lse,
+                         int B, int H, const int32_t* kv_indptr, float scale, void* stream) {
+  bool nothing = false;
+  int st = check_mla(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, &nothing);
+  if (st != TATTN_OK || nothing) return st;
   int cus = 0;
-  int st = current_device_cus(&cus);
-  if (st != TATTN_OK) return st;
+  if ((st = current_device_cus(&cus)) != TATTN_OK) return st;
   const size_t bytes = tattn::mla_workspace_bytes(B, H, cus);
   if (const char* cap = std::getenv("TATTN_WS_LIMIT_BYTES")) {
     if (bytes > (size_t)std::strtoull(cap, nullptr, 10)) return TATTN_ERR_OOM;
@@ -174,6 +186,21 @@ TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const 
   const hipError_t er = hipEventRecord(w.done, s);
   if (e != hipSuccess) return status_of(e);
   return status_of(er);
+}
+
+TATTN_API int mla_decode_noalloc(const void* q, const void* q_pe, const void* kv, const void* k_pe, void* o,
+                                 float* lse, int B, int H, const int32_t* kv_indptr, float scale, void* stream) {
+  bool nothing = false;
+  int st = check_mla(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, &nothing);
+  if (st != TATTN_OK || nothing) return st;
+  int cus = 0;
+  if ((st = current_device_cus(&cus)) != TATTN_OK) return st;
+  if (tattn::mla_workspace_bytes(B, H, cus) > tattn::kNoAllocScratchBytes) return TATTN_ERR_SCRATCH;
+  void* ws = nullptr;
+  const hipError_t e = tattn::mla_noalloc_scratch(&ws);
+  if (e != hipSuccess) return status_of(e);
+  return status_of(tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, cus, ws,
+                                            (hipStream_t)stream));
 }
 
 TATTN_API int ssd_scan(const void* x, const float* dt, const float* A, const void* B, const void* C, void* y,
@@ -210,6 +237,7 @@ TATTN_API const char* tattn_status_str(int status) {
     case TATTN_ERR_ALIGN: return "pointer misaligned";
     case TATTN_ERR_OOM: return "device workspace allocation failed";
     case TATTN_ERR_HIP: return "HIP runtime error or no usable device";
+    case TATTN_ERR_SCRATCH: return "request needs more than the static scratch of mla_decode_noalloc";
     default: return "unknown status";
   }
 }
