@@ -27,28 +27,47 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 N_COPIES = 3
 
-# HBM traffic per launch of the non-causal prefill kernel, from two
-# rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch),
-# each scaled by what the same counter reads for a plain 256 MiB device copy
-# in the same run (FETCH_SIZE read 131093 KiB for it: factor 2.0; WRITE_SIZE
-# read 262144 KiB: factor 1.0). The figures hold for the kernel sources they
-# were taken on; once those files change the field is reported as null.
-TRAFFIC_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip",
-                   "tiled_attention_12_amd/csrc/device_common.h")
-TRAFFIC = {"sources_sha256": "979f09dacadac8051c6f89ecce812fde0d00c6870cf60956149b5d30294cb98a",
-           "fetch_kib": 82129.5, "fetch_factor": 2.0, "write_kib": 33301.7, "write_factor": 1.0}
+# HBM traffic per launch, from two rocprofv3 --pmc passes (FETCH_SIZE, then
+# WRITE_SIZE; KiB per dispatch, summed over the kernels of one call), each
+# scaled by what the same counter reads for a plain 256 MiB device copy in the
+# same run (FETCH_SIZE read 131093 KiB for it: factor 2.0; WRITE_SIZE read
+# 262144 KiB: factor 1.0). A figure holds for the kernel sources it was taken
+# on; once those files change it is reported as null.
+MHA_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip", "tiled_attention_12_amd/csrc/device_common.h")
+MLA_SOURCES = ("tiled_attention_12_amd/csrc/mla_decode.hip", "tiled_attention_12_amd/csrc/device_common.h")
+TRAFFIC = {
+    "mha_prefill_bf16": {"sources": MHA_SOURCES,
+                         "sources_sha256": "979f09dacadac8051c6f89ecce812fde0d00c6870cf60956149b5d30294cb98a",
+                         "fetch_kib": 82129.5, "write_kib": 33301.7},
+    "mha_long_causal_bf16": {"sources": MHA_SOURCES, "sources_sha256": None, "fetch_kib": None, "write_kib": None},
+    "mla_decode_bf16": {"sources": MLA_SOURCES, "sources_sha256": None, "fetch_kib": None, "write_kib": None},
+    "mla_decode_ragged_bf16": {"sources": MLA_SOURCES, "sources_sha256": None, "fetch_kib": None,
+                               "write_kib": None},
+}
+FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
 
-def _traffic_bytes():
-    """Counter-measured HBM bytes per launch, or None if the kernel changed since."""
+def _sources_sha(files):
     import hashlib
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in files:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
-    if h.hexdigest() != TRAFFIC["sources_sha256"]:
+    return h.hexdigest()
+
+
+def _traffic_bytes(name):
+    """Counter-measured HBM bytes per call of a workload, or None if not
+    measured or the kernels changed since."""
+    t = TRAFFIC.get(name)
+    if not t or t["fetch_kib"] is None or _sources_sha(t["sources"]) != t["sources_sha256"]:
         return None
-    return 1024.0 * (TRAFFIC["fetch_kib"] * TRAFFIC["fetch_factor"] + TRAFFIC["write_kib"] * TRAFFIC["write_factor"])
+    return 1024.0 * (t["fetch_kib"] * FETCH_FACTOR + t["write_kib"] * WRITE_FACTOR)
+
+
+def _roofline(bound, achieved, peak, unit, traffic, kernel, alg_per_launch):
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+            "traffic": traffic, "kernel": kernel, "alg_per_launch": alg_per_launch}
 
 
 def _log(msg):
@@ -184,6 +203,95 @@ def _cpu_baseline(budget_s=12.0):
                       f"(alternating non-causal/causal), {dt:.1f} s of float64 numpy on the host"}
 
 
+def _host_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
+    except Exception:  # noqa: BLE001
+        return len(os.sched_getaffinity(0))
+
+
+def _cpu_baselines(budget_s=5.0):
+    """The CPU oracle, as it stands, timed on a bounded sample of each of the
+    five configurations (about budget_s seconds of host work each), in the
+    metric's units: TFLOP/s of the two contractions for the prefill
+    configurations, GB/s of key rows (and TFLOP/s) for the decode ones."""
+    import oracle
+    from tiled_attention_12_amd import inputs
+    from tiled_attention_12_amd.workloads import WORKLOADS, mha_flops, mla_flops
+    out = {}
+    cores = _host_threads()
+
+    def timed(fn, units, done):
+        n, work, t0 = 0, 0.0, time.perf_counter()
+        while time.perf_counter() - t0 < budget_s and not done(n):
+            work += units(n)
+            fn(n)
+            n += 1
+        return n, work, time.perf_counter() - t0
+
+    w = WORKLOADS["mha_tiny_f32"]
+    x = inputs.mha_inputs(w["B"], w["H"], w["Sq"], w["Skv"], w["D"], seed=w["seed"], dtype="f32")
+    f1 = mha_flops(w["B"], w["H"], w["Sq"], w["Skv"], w["D"], False)
+    n, fl, dt = timed(lambda i: oracle.attention(x["q"], x["k"], x["v"], w["scale"]), lambda i: f1,
+                      lambda i: i >= 2000)
+    out["config1_mha_tiny_f32"] = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+                                   "sample": f"{n} whole calls of the workload, {dt:.1f} s"}
+
+    w = WORKLOADS["mha_prefill_bf16"]
+    x = inputs.mha_inputs(1, 4, w["Sq"], w["Skv"], w["D"], seed=w["seed"], sigma=w["sigma"])
+    q, k, v = (inputs.stored_values(x[n]) for n in "qkv")
+    for causal in (False, True):
+        fh = mha_flops(1, 1, w["Sq"], w["Skv"], w["D"], causal)
+        n, fl, dt = timed(lambda i: oracle.attention(q[:, i % 4:i % 4 + 1], k[:, i % 4:i % 4 + 1],
+                                                     v[:, i % 4:i % 4 + 1], w["scale"], causal=causal),
+                          lambda i: fh, lambda i: i >= 64)
+        out[f"config2_mha_prefill_bf16_{'causal' if causal else 'noncausal'}"] = {
+            "value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n} whole (batch, head) slices of the S=2048, D=128 prefill, {dt:.1f} s"}
+    del q, k, v, x
+
+    w = WORKLOADS["mha_long_causal_bf16"]
+    x = inputs.mha_inputs(w["B"], w["H"], w["Sq"], w["Skv"], w["D"], seed=w["seed"], sigma=w["sigma"])
+    S = w["Sq"]
+    rows_per = 2048
+    q, k, v = (inputs.stored_values(x[n][:, :1]) for n in "qkv")
+    del x
+
+    def blk(i):
+        r0 = (i * rows_per) % S
+        oracle.attention(q, k, v, w["scale"], causal=True, rows=np.arange(r0, r0 + rows_per))
+    pairs = lambda i: int(np.sum(np.arange((i * rows_per) % S, (i * rows_per) % S + rows_per) + 1))
+    n, pr, dt = timed(blk, pairs, lambda i: i >= S // rows_per)
+    out["config3_mha_long_causal_bf16"] = {
+        "value": 4 * w["D"] * pr / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+        "sample": f"{n} blocks of {rows_per} query rows of head 0 of the S=16384 causal prefill, {dt:.1f} s"}
+    del q, k, v
+
+    for key, name in (("config4_mla_decode_bf16", "mla_decode_bf16"),
+                      ("config5_mla_decode_ragged_bf16", "mla_decode_ragged_bf16")):
+        w = WORKLOADS[name]
+        kw = {"kv_len": w["kv_len"]} if "kv_len" in w else {"kv_len_range": w["kv_len_range"]}
+        m = inputs.mla_inputs(w["B"], w["H"], seed=w["seed"], sigma=w["sigma"], **kw)
+        ind = m["indptr"]
+        vals = {n: m[n] for n in ("q", "q_pe", "kv", "k_pe")}
+        lens = np.diff(ind)
+
+        def one(i):
+            b = i % w["B"]
+            lo, hi = int(ind[b]), int(ind[b + 1])
+            oracle.mla_decode(inputs.stored_values(vals["q"][b:b + 1]), inputs.stored_values(vals["q_pe"][b:b + 1]),
+                              inputs.stored_values(vals["kv"][lo:hi]), inputs.stored_values(vals["k_pe"][lo:hi]),
+                              np.array([0, hi - lo], np.int64), w["scale"])
+        n, keys, dt = timed(one, lambda i: int(lens[i % w["B"]]), lambda i: i >= w["B"])
+        keys = int(keys)
+        out[key] = {"value": 1152 * keys / dt / 1e9, "unit": "GB/s of key rows", "cores": cores, "kind": "oracle",
+                    "tflops": mla_flops(w["H"], keys) / dt / 1e12,
+                    "sample": f"{n} whole batches ({keys} keys, all {w['H']} heads), {dt:.1f} s"}
+        del m, vals
+    return out
+
+
 def _profile_only(args, ta, dev):
     """Run args.steps launches of one workload (after args.warmup) and print its mean time."""
     import torch
@@ -306,9 +414,12 @@ def main():
             lambda s: ta.attn_fwd(s["q"], s["k"], s["v"], causal=True, scale=w3["scale"], out=o3, lse=l3),
             sets3, 2, 10)
         f3 = mha_flops(w3["B"], w3["H"], w3["Sq"], w3["Skv"], w3["D"], True)
-        workloads["mha_long_causal_bf16"] = {"ms": mean3, "ms_median": med3, "ms_min": min3,
-                                             "tflops": f3 / (mean3 * 1e-3) / 1e12,
-                                             "frac_mfma_peak": f3 / (mean3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS}
+        workloads["mha_long_causal_bf16"] = {
+            "ms": mean3, "ms_median": med3, "ms_min": min3, "tflops": f3 / (mean3 * 1e-3) / 1e12,
+            "frac_mfma_peak": f3 / (mean3 * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "roofline": _roofline("mfma", f3 / (mean3 * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                  _traffic_bytes("mha_long_causal_bf16"),
+                                  "mha_fwd_bf16_kernel<128, 8, 64, 3, true, false> (causal)", f3)}
         del sets3, o3, l3
 
         from tiled_attention_12_amd import inputs
@@ -364,7 +475,12 @@ def main():
                                "kv_gbs": 1152 * total / (mean_m * 1e-3) / 1e9,
                                "alg_gbs": by / (mean_m * 1e-3) / 1e9,
                                "tflops": fl / (mean_m * 1e-3) / 1e12,
-                               "frac_roofline": t_star / (mean_m * 1e-3)}
+                               "frac_roofline": t_star / (mean_m * 1e-3),
+                               # one call = the split kernel and the merge kernel; HBM-bound
+                               # (arithmetic intensity below the ridge point)
+                               "roofline": _roofline("hbm", by / (mean_m * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s",
+                                                     _traffic_bytes(name),
+                                                     "mla_split_kernel<4, 4, true> + mla_combine_kernel", by)}
             del setsm, om, lm
 
         _log("bench: ssd_scan_bf16")
@@ -399,7 +515,7 @@ def main():
         "config": {"workload": "mha_prefill_bf16: B=4 H=16 Sq=Skv=2048 D=128, non-causal + causal per step",
                    "global_batch": B, "seq_len": S, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": _traffic_bytes(),
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": _traffic_bytes("mha_prefill_bf16"),
                      "kernel": "mha_fwd_bf16_kernel<128, 8, 64, 3, false, false> (non-causal)",
                      "alg_flops_per_launch": f_nc, "alg_bytes_per_launch": nbytes},
         "workloads": workloads,
@@ -407,6 +523,8 @@ def main():
     if not args.no_cpu_baseline:
         _log("bench: CPU oracle baseline")
         line["cpu_baseline"] = _cpu_baseline()
+        _log("bench: CPU oracle baseline per configuration")
+        line["cpu_baseline_per_config"] = _cpu_baselines()
     print(json.dumps(line), flush=True)
 
 

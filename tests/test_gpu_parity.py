@@ -380,3 +380,58 @@ def test_mla_running_max_rises_across_tiles(ta, dev, H):
     o, lse = _run_mla(ta, dev, m, scale)
     ro, rl = oracle.mla_decode(*_mla_vals(m), indptr, scale)
     assert_bf16_parity(o, lse, ro, rl, f"mla score ramp H={H}")
+
+
+# ------------------------------------------------------------------ split count, workspace cap
+
+def _ragged_mla(dev, lens, H, seed):
+    m = inputs.mla_inputs(len(lens), H, seed=seed, kv_len=1)
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n = max(int(indptr[-1]), 1)
+    g = np.random.default_rng(seed + 1)
+    m["kv"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 512), dtype=np.float32) * np.float32(0.3))
+    m["k_pe"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 64), dtype=np.float32) * np.float32(0.3))
+    m["indptr"] = indptr
+    return m
+
+
+@pytest.mark.parametrize("H", [64, 128])
+def test_mla_result_does_not_depend_on_the_split_count(ta, dev, H, monkeypatch):
+    # TATTN_MLA_SPLITS replaces the compute-unit count as the number of split
+    # workgroups: one workgroup for everything, a few, and more workgroups than
+    # compute units all agree with the oracle and with the default split
+    lens = [3000, 1, 777, 0, 4096, 65]
+    m = _ragged_mla(dev, lens, H, 51 + H)
+    scale = float(np.float32(576 ** -0.5))
+    ro, rl = oracle.mla_decode(*_mla_vals(m), m["indptr"], scale)
+    o0, l0 = _run_mla(ta, dev, m, scale)
+    for splits in (1, 3, 7, 64, 300, 1000):
+        monkeypatch.setenv("TATTN_MLA_SPLITS", str(splits))
+        o, lse = _run_mla(ta, dev, m, scale)
+        assert_bf16_parity(o, lse, ro, rl, f"mla H={H} splits={splits}")
+        assert np.abs(o - o0).max() <= 1e-2 and np.abs(lse - l0).max() <= 1e-3
+        empty = np.array(lens) == 0
+        assert np.all(o[empty] == 0) and np.all(np.isneginf(lse[empty]))
+    monkeypatch.delenv("TATTN_MLA_SPLITS")
+
+
+def test_mla_workspace_cap_reports_oom_and_writes_nothing(ta, dev, monkeypatch):
+    # a cap below the workspace the call needs: TATTN_ERR_OOM before any
+    # launch, outputs untouched
+    from tiled_attention_12_amd._binding import TattnError, TATTN_ERR_OOM
+    m = _ragged_mla(dev, [500, 20], 128, 61)
+    args = [to_dev(m[n], dev) for n in ("q", "q_pe", "kv", "k_pe")]
+    ind = to_dev(m["indptr"], dev)
+    out = torch.full((2, 128, 512), 3.0, dtype=torch.bfloat16, device=dev)
+    lse = torch.full((2, 128), 3.0, dtype=torch.float32, device=dev)
+    monkeypatch.setenv("TATTN_WS_LIMIT_BYTES", "4096")
+    with pytest.raises(TattnError) as err:
+        ta.mla_decode(*args, ind, 0.05, out=out, lse=lse)
+    assert err.value.status == TATTN_ERR_OOM
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 3.0)) and bool(torch.all(lse == 3.0))
+    monkeypatch.delenv("TATTN_WS_LIMIT_BYTES")
+    o, l2 = ta.mla_decode(*args, ind, 0.05, out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.mla_decode(*_mla_vals(m), m["indptr"], 0.05)
+    assert_bf16_parity(to_np(o), to_np(l2), ro, rl, "mla after the capped call")

@@ -126,6 +126,17 @@ TATTN_API int attn_fwd_f32(const float* q, const float* k, const float* v, float
                                              (hipStream_t)stream));
 }
 
+// Number of split workgroups of the MLA decode: the device's compute units,
+// or TATTN_MLA_SPLITS when set to a positive count (a test hook: the result
+// must not depend on how the keys are split).
+static int mla_splits(int cus) {
+  if (const char* v = std::getenv("TATTN_MLA_SPLITS")) {
+    const long n = std::strtol(v, nullptr, 10);
+    if (n > 0 && n <= 65536) return (int)n;
+  }
+  return cus;
+}
+
 // Shared validation of the two MLA entry points. Returns TATTN_OK with
 // *nothing = true when there is no work.
 static int check_mla(const void* q, const void* q_pe, const void* kv, const void* k_pe, const void* o,
@@ -153,7 +164,8 @@ TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const 
   if (st != TATTN_OK || nothing) return st;
   int cus = 0;
   if ((st = current_device_cus(&cus)) != TATTN_OK) return st;
-  const size_t bytes = tattn::mla_workspace_bytes(B, H, cus);
+  const int n_split = mla_splits(cus);
+  const size_t bytes = tattn::mla_workspace_bytes(B, H, n_split);
   if (const char* cap = std::getenv("TATTN_WS_LIMIT_BYTES")) {
     if (bytes > (size_t)std::strtoull(cap, nullptr, 10)) return TATTN_ERR_OOM;
   }
@@ -182,7 +194,8 @@ TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const 
   } else if (hipStreamWaitEvent(s, w.done, 0) != hipSuccess) {
     return TATTN_ERR_HIP;
   }
-  const hipError_t e = tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, cus, w.ptr, s);
+  const hipError_t e =
+      tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, n_split, w.ptr, s);
   const hipError_t er = hipEventRecord(w.done, s);
   if (e != hipSuccess) return status_of(e);
   return status_of(er);
@@ -195,11 +208,12 @@ TATTN_API int mla_decode_noalloc(const void* q, const void* q_pe, const void* kv
   if (st != TATTN_OK || nothing) return st;
   int cus = 0;
   if ((st = current_device_cus(&cus)) != TATTN_OK) return st;
-  if (tattn::mla_workspace_bytes(B, H, cus) > tattn::kNoAllocScratchBytes) return TATTN_ERR_SCRATCH;
+  const int n_split = mla_splits(cus);
+  if (tattn::mla_workspace_bytes(B, H, n_split) > tattn::kNoAllocScratchBytes) return TATTN_ERR_SCRATCH;
   void* ws = nullptr;
   const hipError_t e = tattn::mla_noalloc_scratch(&ws);
   if (e != hipSuccess) return status_of(e);
-  return status_of(tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, cus, ws,
+  return status_of(tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, n_split, ws,
                                             (hipStream_t)stream));
 }
 
