@@ -73,14 +73,16 @@ def test_more_than_one_gpu_is_refused():
 
 def test_traffic_is_null_once_the_kernel_sources_change(monkeypatch):
     import bench
-    t = bench._traffic_bytes()
-    if t is not None:
-        tr = bench.TRAFFIC
-        assert t == pytest.approx(1024 * (tr["fetch_kib"] * tr["fetch_factor"] + tr["write_kib"] * tr["write_factor"]))
-        # the written bytes can never be fewer than O (bf16) and LSE (fp32) of the headline launch
-        assert tr["write_kib"] * tr["write_factor"] * 1024 >= 4 * 16 * 2048 * (128 * 2 + 4)
-    monkeypatch.setitem(bench.TRAFFIC, "sources_sha256", "0" * 64)
-    assert bench._traffic_bytes() is None
+    for name, tr in bench.TRAFFIC.items():
+        t = bench._traffic_bytes(name)
+        if t is not None:
+            assert t == pytest.approx(1024 * (tr["fetch_kib"] * bench.FETCH_FACTOR + tr["write_kib"] * bench.WRITE_FACTOR))
+        monkeypatch.setitem(tr, "sources_sha256", "0" * 64)
+        assert bench._traffic_bytes(name) is None
+    # the written bytes of the headline launch can never be fewer than O (bf16) and LSE (fp32)
+    tr = bench.TRAFFIC["mha_prefill_bf16"]
+    assert tr["write_kib"] * bench.WRITE_FACTOR * 1024 >= 4 * 16 * 2048 * (128 * 2 + 4)
+    assert bench._traffic_bytes("no such workload") is None
 
 
 def test_cpu_baseline_budget_is_bounded(monkeypatch):
