@@ -39,10 +39,16 @@ TRAFFIC = {
     "mha_prefill_bf16": {"sources": MHA_SOURCES,
                          "sources_sha256": "979f09dacadac8051c6f89ecce812fde0d00c6870cf60956149b5d30294cb98a",
                          "fetch_kib": 82129.5, "write_kib": 33301.7},
-    "mha_long_causal_bf16": {"sources": MHA_SOURCES, "sources_sha256": None, "fetch_kib": None, "write_kib": None},
-    "mla_decode_bf16": {"sources": MLA_SOURCES, "sources_sha256": None, "fetch_kib": None, "write_kib": None},
-    "mla_decode_ragged_bf16": {"sources": MLA_SOURCES, "sources_sha256": None, "fetch_kib": None,
-                               "write_kib": None},
+    "mha_long_causal_bf16": {"sources": MHA_SOURCES,
+                             "sources_sha256": "979f09dacadac8051c6f89ecce812fde0d00c6870cf60956149b5d30294cb98a",
+                             "fetch_kib": 815383.2, "write_kib": 133120.8},
+    # split + merge kernel of one call
+    "mla_decode_bf16": {"sources": MLA_SOURCES,
+                        "sources_sha256": "e040302fce5bd5b3618677a51075bf9f0cda3d796d2c2530c72e001b87212da5",
+                        "fetch_kib": 152246.6 + 16498.3, "write_kib": 32896.3 + 8225.3},
+    "mla_decode_ragged_bf16": {"sources": MLA_SOURCES,
+                               "sources_sha256": "e040302fce5bd5b3618677a51075bf9f0cda3d796d2c2530c72e001b87212da5",
+                               "fetch_kib": 667553.2 + 24533.0, "write_kib": 48959.0 + 16449.6},
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
