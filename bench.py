@@ -413,6 +413,21 @@ def main():
     del sets
 
     if not args.skip_secondary:
+        _log("bench: tiny fp32 attention")
+        from tiled_attention_12_amd import inputs as _inputs
+        from tiled_attention_12_amd.workloads import WORKLOADS as _W
+        w1 = _W["mha_tiny_f32"]
+        x1 = _inputs.mha_inputs(w1["B"], w1["H"], w1["Sq"], w1["Skv"], w1["D"], seed=w1["seed"],
+                                sigma=w1["sigma"], dtype="f32")
+        sets1 = _copies(x1, dev)
+        o1, l1 = ta.attn_fwd_f32(sets1[0]["q"], sets1[0]["k"], sets1[0]["v"], scale=w1["scale"])
+        mean1, med1, min1 = _time_launches(
+            lambda s: ta.attn_fwd_f32(s["q"], s["k"], s["v"], scale=w1["scale"], out=o1, lse=l1), sets1, 5, 50)
+        f1 = mha_flops(w1["B"], w1["H"], w1["Sq"], w1["Skv"], w1["D"], False)
+        workloads["mha_tiny_f32"] = {"ms": mean1, "ms_median": med1, "ms_min": min1,
+                                     "tflops": f1 / (mean1 * 1e-3) / 1e12}
+        del sets1, o1, l1
+
         _log("bench: long causal prefill")
         w3, sets3 = _mha_workload(ta, dev, "mha_long_causal_bf16")
         o3, l3 = ta.attn_fwd(sets3[0]["q"], sets3[0]["k"], sets3[0]["v"], causal=True, scale=w3["scale"])
