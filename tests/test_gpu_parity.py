@@ -356,6 +356,27 @@ def test_bf16_running_max_rises_across_tiles(ta, dev):
         assert_bf16_parity(o, lse, ro, rl, f"score ramp causal={causal}")
 
 
+@pytest.mark.parametrize("jump", [24.0, 200.0, -200.0])
+def test_running_max_jumps_inside_the_sequence(ta, dev, jump):
+    # from key 640 on, one query/key dimension adds `jump` base-2 units to
+    # every score: exponentials taken against the running max of the keys
+    # before would reach 2^24 or overflow to inf (or, for a drop, underflow
+    # to 0), so the step has to detect it and take the exact tile max
+    B, H, S, D = 1, 2, 1000, 128
+    x = inputs.mha_inputs(B, H, S, S, D, seed=44)
+    q = inputs.stored_values(x["q"]).copy()
+    k = inputs.stored_values(x["k"]).copy()
+    scale = float(np.float32(D ** -0.5))
+    q[..., 0] = 1.0
+    k[..., 0] = 0.0
+    k[..., 640:, 0] = jump * np.log(2.0) / scale
+    y = dict(x, q=inputs.f32_to_bf16_bits(q), k=inputs.f32_to_bf16_bits(k))
+    for causal in (False, True):
+        o, lse = _run_mha(ta, dev, y, causal, scale)
+        ro, rl = oracle.attention(*_vals(y, "qkv"), scale, causal=causal)
+        assert_bf16_parity(o, lse, ro, rl, f"score jump {jump} causal={causal}")
+
+
 @pytest.mark.parametrize("H", [32, 64, 128])
 def test_mla_running_max_rises_across_tiles(ta, dev, H):
     # the rotary part carries a score ramp along each batch's keys (about 9

@@ -189,6 +189,16 @@ __device__ __forceinline__ float sum_halves(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Sum of x over the 8 lanes of an aligned lane octet (every lane gets it):
+// xor 1 and xor 2 inside each quad (DPP quad permutes), then the mirror
+// inside each half-row pairs every lane of one quad with a lane of the other.
+__device__ __forceinline__ float octet_sum(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+  return x;
+}
+
 // x *= alpha for an MFMA accumulator that lives in AGPRs, element by element
 // through one temporary VGPR (VALU cannot read AGPRs directly), so a rare
 // rescale of a large accumulator never needs a block of VGPRs.

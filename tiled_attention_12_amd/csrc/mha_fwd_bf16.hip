@@ -345,6 +345,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       });
     };
 
+    bool redo_rows = false;  // this wave's rows need the exact recompute
     if constexpr (EXT) {
       // Sliding window and/or block mask: the workgroup walks only the key
       // tiles that some of its rows can see and that the block mask keeps,
@@ -421,6 +422,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       // every stage offset and register set is a compile-time constant. The
       // refill issued at barrier t targets stage (t+PF) % NSTAGE, last read by
       // P*V of tile t-2 before that barrier.
+      //
+      // These steps take the running max from tile 0 only and exponentiate the
+      // later tiles against it without forming their tile maxima: the same
+      // softmax as long as nothing overflows (a later score would have to
+      // exceed the reference by about 2^7 base-2 units). The epilogue checks
+      // l and O for that and, if needed, runs the item again with the exact
+      // step (tile max, threshold raise, O rescale) on every tile.
       f32x16 sb[2][KB];
       f32x16 (&s_cur)[KB] = sb[0];
       int t_plain = Skv / BC;
@@ -434,6 +442,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         barrier();
         if (PF < nt) issue(PF, std::integral_constant<int, PF % NSTAGE>{});
         m1(std::integral_constant<int, 0>{}, sb[0]);
+        // the reference: tile 0's max (no key of a pipelined tile is masked,
+        // so it is finite for every row)
+        vmax(0, sb[0], std::false_type{});
         for (int t0 = 0; t0 + 1 < t_main; t0 += UN) {
           static_for<UN>([&](auto Uc) {
             constexpr int U = decltype(Uc)::value + 1;          // tile t0 + U
@@ -445,7 +456,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             wait_lgkmcnt0();
             barrier();
             if (t + PF < nt) issue(t + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
-            vmax(t - 1, sb[BP], std::false_type{});
             bf16x8 pf[KB][2];
             vexp(sb[BP], pf);
             m1(std::integral_constant<int, ST>{}, sb[BN]);
@@ -499,6 +509,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         });
       }
 
+      // Overflow check of the first run: l of this lane below 2^100 and every
+      // O accumulator finite (x*0 is NaN for x = inf or NaN). A wave that
+      // fails it writes its rows once more after the epilogue, exactly.
+      {
+        float fin = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) fin = fmaf(oacc[db][i], 0.f, fin);
+        redo_rows = __builtin_amdgcn_ballot_w64(!(lsum <= 0x1p100f) || !(fin == 0.f)) != 0;
+      }
     }
 
     // ---- epilogue: O = acc / l (bf16), LSE = (m + log2 l) * ln 2. The
@@ -541,6 +562,85 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
       if (row < Sq && hi == 0) a.lse[(size_t)bh * Sq + row] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
+
+    // ---- exact recompute of this wave's 32 rows, for a wave whose check
+    // failed: fp32 online softmax with the exact running max, K and V read
+    // straight from global memory, 8 lanes per row (lane r of a row owns the
+    // 16-byte chunks r, r + 8, ...), 8 rows at a time; the results replace
+    // what the epilogue wrote. Slow, and only taken when a later score
+    // exceeds tile 0's max by about 2^7 base-2 units.
+    if (redo_rows) {
+      wait_vmcnt<0>();  // the epilogue's stores of these rows come first
+      constexpr int CL = CPR / 8;  // chunks per lane
+      const int sub = lane & 7;
+      for (int pass = 0; pass < 4; ++pass) {
+        const int r = wrow0 + 8 * pass + (lane >> 3);
+        const int rc = min(r, Sq - 1);
+        const int lim = CAUSAL ? min(Skv - 1, rc + Skv - Sq) : Skv - 1;
+        int lim_w = lim;  // the pass's last key: the largest limit of its rows
+#pragma unroll
+        for (int off = 8; off < 64; off <<= 1) lim_w = max(lim_w, __shfl_xor(lim_w, off));
+        float qv[CL][8], ov[CL][8];
+#pragma unroll
+        for (int ci = 0; ci < CL; ++ci) {
+          const u32x4 w = *(const u32x4*)(qp + (size_t)rc * D + 8 * (sub + 8 * ci));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qv[ci][2 * e] = __uint_as_float(w[e] << 16);
+            qv[ci][2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+            ov[ci][2 * e] = ov[ci][2 * e + 1] = 0.f;
+          }
+        }
+        float mr = -INFINITY, lr = 0.f;
+        for (int j = 0; j <= lim_w; ++j) {
+          const uint16_t* kr = (const uint16_t*)kp + (size_t)j * D;
+          const uint16_t* vr = (const uint16_t*)vp + (size_t)j * D;
+          float dot = 0.f;
+#pragma unroll
+          for (int ci = 0; ci < CL; ++ci) {
+            const u32x4 w = *(const u32x4*)(kr + 8 * (sub + 8 * ci));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              dot = fmaf(qv[ci][2 * e], __uint_as_float(w[e] << 16), dot);
+              dot = fmaf(qv[ci][2 * e + 1], __uint_as_float(w[e] & 0xffff0000u), dot);
+            }
+          }
+          dot = octet_sum(dot);
+          if (j > lim) continue;
+          const float sc = dot * c;
+          if (sc > mr) {
+            const float alpha = fast_exp2(mr - sc);  // 0 for mr = -inf
+            lr *= alpha;
+#pragma unroll
+            for (int ci = 0; ci < CL; ++ci)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) ov[ci][e] *= alpha;
+            mr = sc;
+          }
+          const float p = fast_exp2(sc - mr);
+          lr += p;
+#pragma unroll
+          for (int ci = 0; ci < CL; ++ci) {
+            const u32x4 w = *(const u32x4*)(vr + 8 * (sub + 8 * ci));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              ov[ci][2 * e] = fmaf(p, __uint_as_float(w[e] << 16), ov[ci][2 * e]);
+              ov[ci][2 * e + 1] = fmaf(p, __uint_as_float(w[e] & 0xffff0000u), ov[ci][2 * e + 1]);
+            }
+          }
+        }
+        if (r < Sq) {
+          const float inv = lr > 0.f ? 1.f / lr : 0.f;
+#pragma unroll
+          for (int ci = 0; ci < CL; ++ci) {
+            const u32x4 w = {pack_bf16x2(ov[ci][0] * inv, ov[ci][1] * inv), pack_bf16x2(ov[ci][2] * inv, ov[ci][3] * inv),
+                             pack_bf16x2(ov[ci][4] * inv, ov[ci][5] * inv), pack_bf16x2(ov[ci][6] * inv, ov[ci][7] * inv)};
+            *(u32x4*)(a.o + ((size_t)bh * Sq + r) * D + 8 * (sub + 8 * ci)) = w;
+          }
+          if (sub == 0) a.lse[(size_t)bh * Sq + r] = lr > 0.f ? (mr + __log2f(lr)) * kLn2 : -INFINITY;
+        }
+      }
+    }
   };
 
   // Items of XCD x are x + 8*local (local < L); workgroup w (XCD w % 8, the
@@ -570,7 +670,8 @@ template <int D, int NW, int BC, bool CAUSAL, bool EXT>
 static hipError_t launch_one(const MhaArgs& a, int n_cu, hipStream_t stream) {
   constexpr int BR = NW * 32;
   constexpr int NSTAGE = TATTN_MHA_STAGES;
-  constexpr size_t lds = 2 * (size_t)NSTAGE * BC * D * 2;
+  // the K and V rings, then one flag per wave
+  constexpr size_t lds = 2 * (size_t)NSTAGE * BC * D * 2 + 4 * NW;
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = mha_fwd_bf16_kernel<D, NW, BC, NSTAGE, CAUSAL, EXT>;
   // Thread-safe one-time opt-in to more than the default dynamic LDS.

@@ -34,16 +34,6 @@ constexpr int kF32R = 8;                 // lanes per query row
 constexpr int kF32NW = 4;                // waves per workgroup
 constexpr int kF32Rows = 64 / kF32R * kF32NW;  // query rows per workgroup
 
-// Sum of x over the 8 lanes of an aligned lane octet (every lane gets it).
-__device__ __forceinline__ float octet_sum(float x) {
-  // xor 1 and xor 2 inside each quad, then the mirror inside each half-row
-  // pairs every lane of one quad with a lane of the other
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-  return x;
-}
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kF32NW) void mha_fwd_f32_kernel(F32Args a) {
   constexpr int BC = 32;
