@@ -141,7 +141,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
  *   k_pe      device, bf16 [N, 64],     16-byte aligned
  *   o         device, bf16 [B, H, 512], 16-byte aligned, written
  *   lse       device, fp32 [B, H],      4-byte aligned, written
- *   B >= 0 (0: nothing to do); H is 32, 64 or 128 (else TATTN_ERR_UNSUPPORTED)
+ *   B >= 0 (0: nothing to do); 1 <= H <= 128 (else TATTN_ERR_UNSUPPORTED)
  *   kv_indptr device, int32 [B+1], 4-byte aligned, read on the device only:
  *             kv_indptr[0] >= 0 and non-decreasing; the caller guarantees
  *             that rows up to kv_indptr[B] exist. A decreasing pair is

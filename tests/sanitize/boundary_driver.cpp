@@ -71,7 +71,7 @@ int main() {
   // mla_decode
   expect("mla null ind", mla_decode(P(16), P(16), P(16), P(16), P(16), F(16), 2, 128, nullptr, 0.05f, nullptr),
          TATTN_ERR_INVALID_ARG);
-  expect("mla H=96", mla_decode(P(16), P(16), P(16), P(16), P(16), F(16), 2, 96, I(16), 0.05f, nullptr),
+  expect("mla H=129", mla_decode(P(16), P(16), P(16), P(16), P(16), F(16), 2, 129, I(16), 0.05f, nullptr),
          TATTN_ERR_UNSUPPORTED);
   expect("mla align", mla_decode(P(16), P(16), P(40), P(16), P(16), F(16), 2, 128, I(16), 0.05f, nullptr),
          TATTN_ERR_ALIGN);
@@ -82,7 +82,7 @@ int main() {
          TATTN_OK);
   expect("mla valid, no device",
          mla_decode(P(16), P(16), P(16), P(16), P(16), F(16), 2, 128, I(16), 0.05f, nullptr), TATTN_ERR_HIP);
-  expect("mla noalloc H=96", mla_decode_noalloc(P(16), P(16), P(16), P(16), P(16), F(16), 2, 96, I(16), 0.05f,
+  expect("mla noalloc H=129", mla_decode_noalloc(P(16), P(16), P(16), P(16), P(16), F(16), 2, 129, I(16), 0.05f,
                                                  nullptr),
          TATTN_ERR_UNSUPPORTED);
   expect("mla noalloc null q", mla_decode_noalloc(nullptr, P(16), P(16), P(16), P(16), F(16), 2, 128, I(16),

@@ -100,8 +100,8 @@ def test_mla_argument_validation(L, fn):
     assert call(ind=None) == INVALID
     assert call(B=-1) == INVALID
     assert call(scale=float("nan")) == INVALID
-    assert call(H=16) == UNSUP
-    assert call(H=96) == UNSUP
+    assert call(H=0) == UNSUP
+    assert call(H=129) == UNSUP
     assert call(kv=40) == ALIGN
     assert call(ind=2) == ALIGN
     assert call(B=0, q=None) == OK

@@ -1,5 +1,5 @@
 """HIP graph capture of the attention entry points that allocate nothing
-(attn_fwd, attn_fwd_ex), on gfx950.
+(attn_fwd, attn_fwd_ex, mla_decode_noalloc), on gfx950.
 
 The graph is replayed several times with eager work and synchronisations in
 between, on new inputs copied into the captured buffers, and every replay
@@ -86,3 +86,32 @@ def test_attn_fwd_ex_in_a_graph(ta, dev):
         return ta.attn_fwd_ex(b["q"], b["k"], b["v"], out=o, lse=lse, **kw)
 
     _capture_and_replay(dev, call, bufs, [{n: to_dev(x[n], dev) for n in "qkv"} for x in xs[1:] + xs[:1]])
+
+
+def test_mla_decode_noalloc_in_a_graph(ta, dev):
+    # the decode without allocations (its workspace is the library's static
+    # array) captured once and replayed on new inputs of the same shapes; the
+    # eager reference is mla_decode with its own workspace, same kernels
+    lens = [700, 33, 0, 2500]
+    B, H = len(lens), 128
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    n = int(indptr[-1])
+    xs = []
+    for i in range(3):
+        m = inputs.mla_inputs(B, H, seed=1400 + i, kv_len=1)
+        g = np.random.default_rng(1410 + i)
+        m["kv"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 512), dtype=np.float32) * np.float32(0.3))
+        m["k_pe"] = inputs.f32_to_bf16_bits(g.standard_normal((n, 64), dtype=np.float32) * np.float32(0.3))
+        xs.append({k: to_dev(m[k], dev) for k in ("q", "q_pe", "kv", "k_pe")})
+    ind = to_dev(indptr, dev)
+    bufs = {k: v.clone() for k, v in xs[0].items()}
+    o = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    scale = float(np.float32(576 ** -0.5))
+
+    def call(b, fresh=False):
+        if fresh:
+            return ta.mla_decode(b["q"], b["q_pe"], b["kv"], b["k_pe"], ind, scale)
+        return ta.mla_decode_noalloc(b["q"], b["q_pe"], b["kv"], b["k_pe"], ind, scale, out=o, lse=lse)
+
+    _capture_and_replay(dev, call, bufs, xs[1:] + xs[:1])

@@ -159,9 +159,9 @@ def test_bf16_deterministic(ta, dev):
 
 # ------------------------------------------------------------------ MLA decode
 
-def _run_mla(ta, dev, m, scale):
+def _run_mla(ta, dev, m, scale, fn="mla_decode"):
     args = [to_dev(m[n], dev) for n in ("q", "q_pe", "kv", "k_pe")]
-    o, lse = ta.mla_decode(*args, to_dev(m["indptr"], dev), scale)
+    o, lse = getattr(ta, fn)(*args, to_dev(m["indptr"], dev), scale)
     torch.cuda.synchronize()
     return to_np(o), to_np(lse)
 
@@ -193,6 +193,21 @@ def test_mla_small(ta, dev, H, lens):
         if L == 0:
             assert np.all(o[b] == 0) and np.all(np.isneginf(lse[b]))
     assert_bf16_parity(o, lse, ro, rl, f"mla H={H} lens={lens}")
+
+
+@pytest.mark.parametrize("fn", ["mla_decode", "mla_decode_noalloc"])
+@pytest.mark.parametrize("H", [1, 16, 33, 48, 96, 100, 127])
+def test_mla_any_head_count(ta, dev, H, fn):
+    # head counts that are not a multiple of 32: the last wave carries padding
+    # heads whose results must not reach O, LSE or the neighbouring partials
+    lens = [1, 300, 0, 2049, 64]
+    m = _ragged_mla(dev, lens, H, seed=50 + H)
+    scale = float(np.float32(576 ** -0.5))
+    o, lse = _run_mla(ta, dev, m, scale, fn=fn)
+    ro, rl = oracle.mla_decode(*_mla_vals(m), m["indptr"], scale)
+    assert o.shape == (len(lens), H, 512) and lse.shape == (len(lens), H)
+    assert np.all(o[2] == 0) and np.all(np.isneginf(lse[2]))
+    assert_bf16_parity(o, lse, ro, rl, f"{fn} H={H}")
 
 
 def test_mla_ragged_batch_equals_standalone(ta, dev):

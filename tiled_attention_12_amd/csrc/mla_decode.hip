@@ -248,7 +248,10 @@ void mla_split_kernel(MlaArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hi = lane >> 5, col = lane & 31;
   const int H = a.H;
+  // heads past H (the last wave's padding when H is not a multiple of 32)
+  // compute on head H-1's query and store nothing
   const int head = wave * 32 + col;
+  const int qhead = min(head, H - 1);
   const float c = a.c;
   const uint32_t smem0 = lds_addr(smem);
 
@@ -358,8 +361,8 @@ void mla_split_kernel(MlaArgs a) {
     // they travel together)
     bf16x8 qf[KS];
     {
-      const uint16_t* qr = a.q + ((size_t)b * H + head) * kDl + hi * 8;
-      const uint16_t* pr = a.qpe + ((size_t)b * H + head) * kDr + hi * 8;
+      const uint16_t* qr = a.q + ((size_t)b * H + qhead) * kDl + hi * 8;
+      const uint16_t* pr = a.qpe + ((size_t)b * H + qhead) * kDr + hi * 8;
 #pragma unroll
       for (int ks = 0; ks < KSL; ++ks) qf[ks] = as_bf16x8(*(const u32x4*)(qr + ks * 16));
 #pragma unroll
@@ -527,10 +530,11 @@ void mla_split_kernel(MlaArgs a) {
                     pack_bf16x2(oacc[db][g4 * 4 + 2] * inv, oacc[db][g4 * 4 + 3] * inv)};
         }
       uint16_t* po = a.part_o + (slot * H + wave * 32) * kDl + 8 * lane;
+      const int rows = min(32, H - wave * 32);  // this wave's heads below H
 #pragma unroll 8
       for (int r = 0; r < 32; ++r)
-        *(u32x4*)(po + (size_t)r * kDl) = *(const lds_u32x4*)(uintptr_t)(stg + r * SRS + 16 * lane);
-      if (hi == 0) a.part_lse[slot * H + head] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+        if (r < rows) *(u32x4*)(po + (size_t)r * kDl) = *(const lds_u32x4*)(uintptr_t)(stg + r * SRS + 16 * lane);
+      if (hi == 0 && head < H) a.part_lse[slot * H + head] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
     }
 
     g = seg_end;
@@ -587,11 +591,10 @@ hipError_t launch_mla_decode(const void* q, const void* q_pe, const void* kv, co
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  switch (H) {
-    case 128: e = fuse ? launch_split<4, 4, true>(a, n_split, stream) : launch_split<4, 4, false>(a, n_split, stream); break;
-    case 64: e = fuse ? launch_split<2, 4, true>(a, n_split, stream) : launch_split<2, 4, false>(a, n_split, stream); break;
-    default: e = fuse ? launch_split<1, 3, true>(a, n_split, stream) : launch_split<1, 3, false>(a, n_split, stream); break;
-  }
+  // 32 heads per wave: 4 waves above 64 heads, 2 above 32, else 1
+  if (H > 64) e = fuse ? launch_split<4, 4, true>(a, n_split, stream) : launch_split<4, 4, false>(a, n_split, stream);
+  else if (H > 32) e = fuse ? launch_split<2, 4, true>(a, n_split, stream) : launch_split<2, 4, false>(a, n_split, stream);
+  else e = fuse ? launch_split<1, 3, true>(a, n_split, stream) : launch_split<1, 3, false>(a, n_split, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3(B, (H + 7) / 8), dim3(256), 0, stream, a, n_split);
   return hipGetLastError();

@@ -148,7 +148,7 @@ static int check_mla(const void* q, const void* q_pe, const void* kv, const void
     *nothing = true;
     return TATTN_OK;
   }
-  if (H != 32 && H != 64 && H != 128) return TATTN_ERR_UNSUPPORTED;
+  if (H < 1 || H > 128) return TATTN_ERR_UNSUPPORTED;
   if (!q || !q_pe || !kv || !k_pe || !o || !lse || !kv_indptr) return TATTN_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(q_pe, 16) || !aligned(kv, 16) || !aligned(k_pe, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(kv_indptr, 4))
