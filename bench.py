@@ -37,18 +37,18 @@ MHA_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip", "tiled_attention_
 MLA_SOURCES = ("tiled_attention_12_amd/csrc/mla_decode.hip", "tiled_attention_12_amd/csrc/device_common.h")
 TRAFFIC = {
     "mha_prefill_bf16": {"sources": MHA_SOURCES,
-                         "sources_sha256": "979f09dacadac8051c6f89ecce812fde0d00c6870cf60956149b5d30294cb98a",
-                         "fetch_kib": 82129.5, "write_kib": 33301.7},
+                         "sources_sha256": "07fc33fe4e931a9dfe381db2208eaeb0a0275f4fc4a9d4164779a29588b5be63",
+                         "fetch_kib": 82117.9, "write_kib": 33317.5},
     "mha_long_causal_bf16": {"sources": MHA_SOURCES,
-                             "sources_sha256": "979f09dacadac8051c6f89ecce812fde0d00c6870cf60956149b5d30294cb98a",
-                             "fetch_kib": 815383.2, "write_kib": 133120.8},
+                             "sources_sha256": "07fc33fe4e931a9dfe381db2208eaeb0a0275f4fc4a9d4164779a29588b5be63",
+                             "fetch_kib": 779237.8, "write_kib": 134146.6},
     # split + merge kernel of one call
     "mla_decode_bf16": {"sources": MLA_SOURCES,
-                        "sources_sha256": "e040302fce5bd5b3618677a51075bf9f0cda3d796d2c2530c72e001b87212da5",
-                        "fetch_kib": 152246.6 + 16498.3, "write_kib": 32896.3 + 8225.3},
+                        "sources_sha256": "98921b8b8318f4b08a5eef2b2054ff5d02ec3ef56c7fc37ca68a6d79eb7ff756",
+                        "fetch_kib": 152249.1 + 16498.4, "write_kib": 32896.3 + 8225.0},
     "mla_decode_ragged_bf16": {"sources": MLA_SOURCES,
-                               "sources_sha256": "e040302fce5bd5b3618677a51075bf9f0cda3d796d2c2530c72e001b87212da5",
-                               "fetch_kib": 667553.2 + 24533.0, "write_kib": 48959.0 + 16449.6},
+                               "sources_sha256": "98921b8b8318f4b08a5eef2b2054ff5d02ec3ef56c7fc37ca68a6d79eb7ff756",
+                               "fetch_kib": 667584.5 + 24533.1, "write_kib": 48959.0 + 16449.8},
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
