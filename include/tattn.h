@@ -14,8 +14,8 @@
  * fully overwritten (never accumulated into). Calls are reentrant and may be
  * issued concurrently on different streams. attn_fwd, attn_fwd_ex,
  * attn_fwd_f32 and ssd_scan allocate nothing and issue only kernel launches,
- * so they may be captured into a HIP graph; mla_decode keeps a device
- * workspace and orders calls with an event (see its description).
+ * so they may be captured into a HIP graph, and so does mla_decode_noalloc;
+ * mla_decode keeps device workspaces per stream (see its description).
  *
  * bf16 tensors are raw IEEE bfloat16 bit patterns (uint16 storage). All
  * tensors are dense, row-major (last index fastest), with no padding.
@@ -153,12 +153,14 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
  * normalised partial output and its log-sum-exp into a device workspace
  * ((CUs + B) * H * (512 * 2 + 4) bytes plus the split plan), and a second
  * kernel merges the pieces of each batch. The library keeps one such
- * workspace per device for the life of the process: a call that needs more
- * than it holds waits for the previous call's kernels, frees it and
- * allocates a larger one with hipMalloc (TATTN_ERR_OOM if that fails); any
- * other call allocates nothing. A call made on a different stream from the
- * previous one first makes its stream wait for that call's kernels, so calls
- * on several streams of one device are correct but run one after another.
+ * workspace per (device, stream) for the life of the process, for up to 8
+ * streams per device: a call that needs more than its stream's workspace
+ * holds allocates a larger one with hipMalloc (TATTN_ERR_OOM if that fails)
+ * and frees the old one at a later call, once that buffer's last kernels
+ * have finished (the host never waits for them); any other call allocates
+ * nothing. Calls on different streams use different workspaces and do not
+ * wait for each other; a ninth stream takes over the least recently used
+ * stream's workspace and first waits for that stream's last call.
  */
 int mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe,
                void* o, float* lse, int B, int H, const int32_t* kv_indptr,

@@ -332,6 +332,31 @@ def test_mla_calls_on_two_streams(ta, dev):
     assert_bf16_parity(to_np(rb[0]), to_np(rb[1]), ro, rl, "mla stream b")
 
 
+def test_mla_streams_beyond_the_workspace_slots(ta, dev):
+    # each stream of a device gets its own decode workspace, up to eight; more
+    # streams take over the least recently used one. Ten streams, each with
+    # growing calls back to back and no synchronisation in between, must all
+    # get the results of a lone call.
+    scale = float(np.float32(576 ** -0.5))
+    cases = [_mla_dev_inputs(dev, 3 + 7 * i, 128 if i % 2 else 64, 60 + i, (1, 300 + 200 * i)) for i in range(10)]
+    ref = []
+    for m, args in cases:
+        ref.append(ta.mla_decode(*args, scale))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(dev) for _ in range(10)]
+    got = []
+    for rep in range(2):
+        for i, (s, (m, args)) in enumerate(zip(streams, cases)):
+            with torch.cuda.stream(s):
+                got.append((i, ta.mla_decode(*args, scale)))
+    torch.cuda.synchronize()
+    for i, (o, l) in got:
+        assert torch.equal(o, ref[i][0]) and torch.equal(l, ref[i][1]), f"stream {i}"
+    m, _ = cases[3]
+    ro, rl = oracle.mla_decode(*_mla_vals(m), m["indptr"], scale)
+    assert_bf16_parity(to_np(ref[3][0]), to_np(ref[3][1]), ro, rl, "mla stream case 3")
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_more_items_than_compute_units_without_xcd_order(ta, dev, causal):
     # B*H = 5 is not a multiple of 8, so items are taken in plain order; 5 heads

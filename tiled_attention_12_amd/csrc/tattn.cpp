@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <mutex>
+#include <vector>
 
 #include "launch.h"
 
@@ -51,18 +52,69 @@ int have_device() {
   return (hipGetDevice(&dev) == hipSuccess && dev >= 0) ? TATTN_OK : TATTN_ERR_HIP;
 }
 
-// Decode workspace of one device: grown (never shrunk) to the largest size a
-// call has needed and kept until the process ends. `done` is recorded on the
-// stream of the last call that used it; the next call's stream waits for it,
-// so calls on different streams never share the buffer at the same time.
+// Decode workspaces: one per (device, stream), up to kWsSlots streams per
+// device, each grown (never shrunk) to the largest size a call on that
+// stream has needed and kept until the process ends. `done` is recorded
+// after each call's kernels; a call first makes its stream wait for the
+// slot's last `done` (free on the same stream; it orders a slot that passes
+// to another stream when every slot is taken). A buffer that has to grow is
+// not freed at once: it is retired with its `done` event and freed by a
+// later call once that event has completed, so no call blocks the host.
 struct Workspace {
+  hipStream_t stream = nullptr;
+  bool used = false;
   void* ptr = nullptr;
   size_t bytes = 0;
   hipEvent_t done = nullptr;
+  unsigned long long last_use = 0;
+};
+struct Retired {
+  void* ptr;
+  hipEvent_t done;
+};
+constexpr int kWsSlots = 8;
+struct DeviceWorkspaces {
+  Workspace slot[kWsSlots];
+  std::vector<Retired> retired;
+  unsigned long long clock = 0;
 };
 
 std::mutex g_ws_mu;
-Workspace g_ws[256];
+DeviceWorkspaces g_ws[256];
+
+// Frees retired buffers whose last kernels have completed (never waits).
+void free_retired(DeviceWorkspaces& d) {
+  size_t keep = 0;
+  for (size_t i = 0; i < d.retired.size(); ++i) {
+    Retired& r = d.retired[i];
+    if (hipEventQuery(r.done) == hipSuccess) {
+      (void)hipFree(r.ptr);
+      (void)hipEventDestroy(r.done);
+    } else {
+      d.retired[keep++] = r;
+    }
+  }
+  d.retired.resize(keep);
+  (void)hipGetLastError();  // a not-ready query is not an error of this call
+}
+
+// The slot of `s` on this device: its own, else an unused one, else the
+// least recently used one (whose stream the call then waits for).
+Workspace& slot_for(DeviceWorkspaces& d, hipStream_t s) {
+  Workspace* lru = &d.slot[0];
+  for (Workspace& w : d.slot) {
+    if (w.used && w.stream == s) return w;
+    if (w.last_use < lru->last_use) lru = &w;
+  }
+  for (Workspace& w : d.slot)
+    if (!w.used) {
+      w.used = true;
+      w.stream = s;
+      return w;
+    }
+  lru->stream = s;
+  return *lru;
+}
 
 // Shared validation of the two MHA entry points. Returns TATTN_OK with
 // *nothing = true when there is no work.
@@ -173,26 +225,35 @@ TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const 
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 256) return TATTN_ERR_HIP;
   hipStream_t s = (hipStream_t)stream;
   std::lock_guard<std::mutex> lock(g_ws_mu);
-  Workspace& w = g_ws[dev];
+  DeviceWorkspaces& d = g_ws[dev];
+  free_retired(d);
+  Workspace& w = slot_for(d, s);
+  w.last_use = ++d.clock;
   if (!w.done && hipEventCreateWithFlags(&w.done, hipEventDisableTiming) != hipSuccess) {
     w.done = nullptr;
     return TATTN_ERR_HIP;
   }
+  // after the slot's last call (a no-op dependency on the same stream)
+  if (hipStreamWaitEvent(s, w.done, 0) != hipSuccess) return TATTN_ERR_HIP;
   if (w.bytes < bytes) {
-    // the old buffer may still be in use by the last call's kernels
-    if (w.ptr) {
-      if (hipEventSynchronize(w.done) != hipSuccess || hipFree(w.ptr) != hipSuccess) return TATTN_ERR_HIP;
-      w.ptr = nullptr;
-      w.bytes = 0;
-    }
-    if (hipMalloc(&w.ptr, bytes) != hipSuccess || !w.ptr) {
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess || !p) {
       (void)hipGetLastError();
-      w.ptr = nullptr;
       return TATTN_ERR_OOM;
     }
+    if (w.ptr) {
+      // the old buffer may still be in use by the slot's last call: retire it
+      // with that call's event, which takes a fresh event for the slot
+      hipEvent_t fresh = nullptr;
+      if (hipEventCreateWithFlags(&fresh, hipEventDisableTiming) != hipSuccess) {
+        (void)hipFree(p);
+        return TATTN_ERR_HIP;
+      }
+      d.retired.push_back({w.ptr, w.done});
+      w.done = fresh;
+    }
+    w.ptr = p;
     w.bytes = bytes;
-  } else if (hipStreamWaitEvent(s, w.done, 0) != hipSuccess) {
-    return TATTN_ERR_HIP;
   }
   const hipError_t e =
       tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, n_split, w.ptr, s);
