@@ -396,13 +396,14 @@ def test_bf16_running_max_rises_across_tiles(ta, dev):
         assert_bf16_parity(o, lse, ro, rl, f"score ramp causal={causal}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("jump", [24.0, 200.0, -200.0])
-def test_running_max_jumps_inside_the_sequence(ta, dev, jump):
+def test_running_max_jumps_inside_the_sequence(ta, dev, jump, D):
     # from key 640 on, one query/key dimension adds `jump` base-2 units to
     # every score: exponentials taken against the running max of the keys
     # before would reach 2^24 or overflow to inf (or, for a drop, underflow
     # to 0), so the step has to detect it and take the exact tile max
-    B, H, S, D = 1, 2, 1000, 128
+    B, H, S = 1, 2, 1000
     x = inputs.mha_inputs(B, H, S, S, D, seed=44)
     q = inputs.stored_values(x["q"]).copy()
     k = inputs.stored_values(x["k"]).copy()
@@ -414,7 +415,27 @@ def test_running_max_jumps_inside_the_sequence(ta, dev, jump):
     for causal in (False, True):
         o, lse = _run_mha(ta, dev, y, causal, scale)
         ro, rl = oracle.attention(*_vals(y, "qkv"), scale, causal=causal)
-        assert_bf16_parity(o, lse, ro, rl, f"score jump {jump} causal={causal}")
+        assert_bf16_parity(o, lse, ro, rl, f"score jump {jump} D={D} causal={causal}")
+
+
+def test_grouped_heads_score_jump(ta, dev):
+    # the grouped-KV path shares the dense kernel's overflow check and exact
+    # recompute: a 200-unit jump in the keys of one KV head
+    B, H, Hkv, S, D = 1, 4, 2, 700, 128
+    x = inputs.mha_inputs(B, H, S, S, D, seed=45, Hkv=Hkv)
+    q = inputs.stored_values(x["q"]).copy()
+    k = inputs.stored_values(x["k"]).copy()
+    scale = float(np.float32(D ** -0.5))
+    q[..., 0] = 1.0
+    k[..., 0] = 0.0
+    k[:, 1, 400:, 0] = 200.0 * np.log(2.0) / scale
+    y = dict(x, q=inputs.f32_to_bf16_bits(q), k=inputs.f32_to_bf16_bits(k))
+    qd, kd, vd = (to_dev(y[n], dev) for n in "qkv")
+    for causal in (False, True):
+        o, lse = ta.attn_fwd_ex(qd, kd, vd, causal=causal, scale=scale)
+        torch.cuda.synchronize()
+        ro, rl = oracle.attention_masked(*_vals(y, "qkv"), scale, causal=causal)
+        assert_bf16_parity(to_np(o), to_np(lse), ro, rl, f"grouped score jump causal={causal}")
 
 
 @pytest.mark.parametrize("H", [32, 64, 128])
