@@ -80,6 +80,15 @@ __device__ __forceinline__ void load_lds16_asm(const void* gptr, uint32_t lds_ba
                :: "v"(gptr), "s"(lds_base_uniform) : "memory", "m0");
 }
 
+// The same load in the instruction's scalar-base form: a wave-uniform 64-bit
+// base address in SGPRs plus a 32-bit unsigned per-lane byte offset, so each
+// load needs one VGPR for its offset and no per-lane 64-bit address add.
+__device__ __forceinline__ void load_lds16_sbase(const void* base_uniform, uint32_t voff,
+                                                 uint32_t lds_base_uniform) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(base_uniform), "s"(lds_base_uniform) : "memory", "m0");
+}
+
 // ds_read_b64_tr_b16 through the compiler builtin (it tracks lgkmcnt and can
 // place the result directly in an MFMA operand tuple).
 template <int OFF>

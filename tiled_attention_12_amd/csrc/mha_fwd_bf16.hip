@@ -175,8 +175,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int row = slot / CPR;
         const uint32_t off = (uint32_t)(min(row, lim) * RS + 16 * swz<CPR>(row, slot % CPR));
         const uint32_t dst = smem0 + ST * TILE + (n * NW + wave) * 1024;
-        load_lds16_asm(kt + off, dst);
-        load_lds16_asm(vt + off, dst + VREG);
+        load_lds16_sbase(kt, off, dst);
+        load_lds16_sbase(vt, off, dst + VREG);
       }
     };
 

@@ -343,15 +343,16 @@ void mla_split_kernel(MlaArgs a) {
       for (int n = 0; n < LAT_LOADS; ++n) {
         const int row = n * NW + wave;
         const int gr = min(key0 + row, kv_hi - 1);
-        load_lds16((const char*)(a.kv + (size_t)gr * kDl) + 16 * lane, sl + row * kRowL);
+        load_lds16_sbase(a.kv + (size_t)gr * kDl, 16 * lane, lds_addr(sl + row * kRowL));
       }
+      // rotary rows relative to the tile's first row (clamped like the latent rows)
+      const int rbase = min(key0, kv_hi - 1);
 #pragma unroll
       for (int n = 0; n < PE_LOADS; ++n) {
         const int slot = (n * NW + wave) * 64 + lane;
         const int row = slot >> 3;
-        const int gr = min(key0 + row, kv_hi - 1);
-        load_lds16((const char*)(a.kpe + (size_t)gr * kDr) + swz<8>(row, slot & 7) * 16,
-                   sl + kTileL + (n * NW + wave) * 1024);
+        const uint32_t voff = (uint32_t)(min(row, kv_hi - 1 - rbase) * (kDr * 2) + swz<8>(row, slot & 7) * 16);
+        load_lds16_sbase(a.kpe + (size_t)rbase * kDr, voff, lds_addr(sl + kTileL + (n * NW + wave) * 1024));
       }
     };
 #pragma unroll
