@@ -37,18 +37,18 @@ MHA_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip", "tiled_attention_
 MLA_SOURCES = ("tiled_attention_12_amd/csrc/mla_decode.hip", "tiled_attention_12_amd/csrc/device_common.h")
 TRAFFIC = {
     "mha_prefill_bf16": {"sources": MHA_SOURCES,
-                         "sources_sha256": "07fc33fe4e931a9dfe381db2208eaeb0a0275f4fc4a9d4164779a29588b5be63",
-                         "fetch_kib": 82117.9, "write_kib": 33317.5},
+                         "sources_sha256": "41d12a59ee22277f05efd699b5678701cfa6c3da8716d6423c8f7f686e4f25d8",
+                         "fetch_kib": 82118.4, "write_kib": 33296.8},
     "mha_long_causal_bf16": {"sources": MHA_SOURCES,
-                             "sources_sha256": "07fc33fe4e931a9dfe381db2208eaeb0a0275f4fc4a9d4164779a29588b5be63",
-                             "fetch_kib": 779237.8, "write_kib": 134146.6},
+                             "sources_sha256": "41d12a59ee22277f05efd699b5678701cfa6c3da8716d6423c8f7f686e4f25d8",
+                             "fetch_kib": 811303.1, "write_kib": 133122.1},
     # split + merge kernel of one call
     "mla_decode_bf16": {"sources": MLA_SOURCES,
-                        "sources_sha256": "98921b8b8318f4b08a5eef2b2054ff5d02ec3ef56c7fc37ca68a6d79eb7ff756",
-                        "fetch_kib": 152249.1 + 16498.4, "write_kib": 32896.3 + 8225.0},
+                        "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
+                        "fetch_kib": 152247.1 + 16498.3, "write_kib": 32896.3 + 8225.4},
     "mla_decode_ragged_bf16": {"sources": MLA_SOURCES,
-                               "sources_sha256": "98921b8b8318f4b08a5eef2b2054ff5d02ec3ef56c7fc37ca68a6d79eb7ff756",
-                               "fetch_kib": 667584.5 + 24533.1, "write_kib": 48959.0 + 16449.8},
+                               "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
+                               "fetch_kib": 667550.4 + 24532.8, "write_kib": 48959.0 + 16449.3},
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
