@@ -82,6 +82,27 @@ def test_wide_sliding_window(ta, dev, D, causal, W):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
+def test_narrow_window_more_items_than_workgroup_slots(ta, dev, D, causal):
+    # 4*16 heads of thirteen 128-row query tiles (the last one ragged): 832 work
+    # items, more than the persistent grid has workgroups (three per compute
+    # unit at head width 64, two at 128), in the XCD order. Outputs are
+    # prefilled with NaN so an item that no workgroup wrote fails; every
+    # element is checked.
+    x = inputs.mha_inputs(4, 16, 1600, 1600, D, seed=995 + D + int(causal))
+    q, k, v = (to_dev(x[n], dev) for n in "qkv")
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
+    scale = float(np.float32(D ** -0.5))
+    ta.attn_fwd_ex(q, k, v, causal=causal, scale=scale, window=100, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o, l = to_np(out), to_np(lse)
+    ro, rl = oracle.attention_masked(*_vals(x, "qkv"), scale, causal=causal, window=100)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    assert_bf16_parity(o, l, ro, rl, f"narrow window many items D={D} causal={causal}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("density", [0.3, 0.7])
 @pytest.mark.parametrize("sq,skv", [(257, 300), (600, 600), (100, 700)])
 def test_block_mask(ta, dev, D, causal, density, sq, skv):

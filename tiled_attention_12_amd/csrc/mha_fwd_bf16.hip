@@ -33,8 +33,8 @@
 //    2^8 (in base-2 units), so the O rescale runs on few tiles; every
 //    exponential stays <= 2^8 and the result is unchanged (both O and l are
 //    taken relative to the same m).
-//  * Persistent grid: one workgroup per compute unit (two for the 4-wave
-//    narrow-window launch) loops over work items (one NW*32-row query tile of
+//  * Persistent grid: one workgroup per compute unit (two or three for the
+//    4-wave narrow-window launch) loops over work items (one NW*32-row query tile of
 //    one (batch, head) each). The hardware hands
 //    workgroup i to XCD i % 8 and item i runs on XCD i % 8 too: all query
 //    tiles of a (batch, head) go to one XCD so its K/V stays in that XCD's
@@ -78,8 +78,15 @@ struct MhaArgs {
 // wave's 32 rows lie inside one query block).
 constexpr int kMaskBlock = 64;
 
+// Waves per SIMD. The 4-wave window/mask walk at head width 64 fits in the
+// 168 registers of three waves per SIMD (three workgroups per compute unit);
+// at head width 128 it would spill there, and a third workgroup then measured
+// slower on narrow windows, so that and every other instantiation run two.
+template <int D, int NW, bool EXT>
+constexpr int kWavesPerSimd = (EXT && NW == 4 && D == 64) ? 3 : 2;
+
 template <int D, int NW, int BC, int NSTAGE, bool CAUSAL, bool EXT>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void mha_fwd_bf16_kernel(MhaArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, NW, EXT>, kWavesPerSimd<D, NW, EXT>))) void mha_fwd_bf16_kernel(MhaArgs a) {
   constexpr int BR = NW * 32;      // query rows per workgroup (32 per wave)
   constexpr int CPR = D / 8;       // 16-byte chunks per row
   constexpr int RS = D * 2;        // row stride in bytes
@@ -684,9 +691,10 @@ static hipError_t launch_one(const MhaArgs& a, int n_cu, hipStream_t stream) {
   if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   b.n_items = (int)items;
   b.remap = (a.n_bh % 8) == 0 && n_cu >= 8;
-  // as many workgroups per compute unit as LDS and two waves per SIMD allow
+  // as many workgroups per compute unit as LDS and the waves per SIMD allow
   // (one for 8-wave workgroups); a multiple of 8 for the XCD order
-  constexpr int OCC = (int)(160 * 1024 / lds) < 8 / NW ? (int)(160 * 1024 / lds) : 8 / NW;
+  constexpr int WG_REG = 4 * kWavesPerSimd<D, NW, EXT> / NW;
+  constexpr int OCC = (int)(160 * 1024 / lds) < WG_REG ? (int)(160 * 1024 / lds) : WG_REG;
   static_assert(OCC >= 1, "one workgroup must fit");
   const long long slots = (long long)n_cu * OCC;
   long long grid = items < slots ? items : slots;
@@ -716,9 +724,9 @@ hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void
   a.nkb = (Skv + kMaskBlock - 1) / kMaskBlock;
   const bool ext = window > 0 || block_mask != nullptr;
   // Narrow windows (at most 768 visible keys per row) run on 4-wave
-  // workgroups of 128 rows with 32-key tiles, two per compute unit, so one
-  // workgroup's loads, item start and output stores overlap the other's
-  // arithmetic; such a window moves more bytes per FLOP than the MFMAs need.
+  // workgroups of 128 rows with 32-key tiles, two per compute unit (three at
+  // head width 64), so one workgroup's loads, item start and output stores
+  // overlap another's arithmetic; such a window moves more bytes per FLOP than the MFMAs need.
   // Wider windows and block masks alone keep the 8-wave, 64-key walk.
   const long long span = causal ? (long long)window + 1 : 2LL * window;
   if (window > 0 && span <= 768) {
