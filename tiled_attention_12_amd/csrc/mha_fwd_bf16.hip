@@ -78,12 +78,19 @@ struct MhaArgs {
 // wave's 32 rows lie inside one query block).
 constexpr int kMaskBlock = 64;
 
-// Waves per SIMD. The 4-wave window/mask walk at head width 64 fits in the
-// 168 registers of three waves per SIMD (three workgroups per compute unit);
-// at head width 128 it would spill there, and a third workgroup then measured
-// slower on narrow windows, so that and every other instantiation run two.
+// Waves per SIMD: three for the 4-wave window/mask walk (three workgroups per
+// compute unit, within the 168 registers that leaves each wave), two for the
+// others.
 template <int D, int NW, bool EXT>
-constexpr int kWavesPerSimd = (EXT && NW == 4 && D == 64) ? 3 : 2;
+constexpr int kWavesPerSimd = (EXT && NW == 4) ? 3 : 2;
+
+// The 4-wave walk at head width 128 takes the lane id through an opaque copy
+// per work item, so its lane-dependent addresses are recomputed per item
+// instead of being held across items: that keeps it within 168 registers
+// (held, they spilled and were reloaded from scratch at every item start).
+// The other instantiations keep them, which measured faster for them.
+template <int D, int NW, bool EXT>
+constexpr bool kLanePerItem = EXT && NW == 4 && D == 128;
 
 template <int D, int NW, int BC, int NSTAGE, bool CAUSAL, bool EXT>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D, NW, EXT>, kWavesPerSimd<D, NW, EXT>))) void mha_fwd_bf16_kernel(MhaArgs a) {
@@ -108,15 +115,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
 
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
-  const int lane = threadIdx.x & 63;
+  const int lane0 = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hi = lane >> 5;      // wave half
-  const int col = lane & 31;     // query column owned by the lane
+  const int hi0 = lane0 >> 5;    // wave half
+  const int col0 = lane0 & 31;   // query column owned by the lane
 
   // One work item = one (batch*head, BR-row query tile). The grid is
   // persistent (as many workgroups as fit on the compute units at once);
   // item i runs where workgroup i would: on XCD i % 8.
   auto process = [&](const int i) {
+    int lane = lane0, hi = hi0, col = col0;
+    if constexpr (kLanePerItem<D, NW, EXT>) {
+      asm volatile("" : "+v"(lane));
+      hi = lane >> 5;
+      col = lane & 31;
+    }
     int bh, qt;
     {
       int rank;
