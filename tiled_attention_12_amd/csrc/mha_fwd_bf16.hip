@@ -33,8 +33,8 @@
 //    2^8 (in base-2 units), so the O rescale runs on few tiles; every
 //    exponential stays <= 2^8 and the result is unchanged (both O and l are
 //    taken relative to the same m).
-//  * Persistent grid: one workgroup per compute unit (two or three for the
-//    4-wave narrow-window launch) loops over work items (one NW*32-row query tile of
+//  * Persistent grid: one workgroup per compute unit (three for the 4-wave
+//    window/mask launch) loops over work items (one NW*32-row query tile of
 //    one (batch, head) each). The hardware hands
 //    workgroup i to XCD i % 8 and item i runs on XCD i % 8 too: all query
 //    tiles of a (batch, head) go to one XCD so its K/V stays in that XCD's
@@ -736,20 +736,15 @@ hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void
   a.nqb = (Sq + kMaskBlock - 1) / kMaskBlock;
   a.nkb = (Skv + kMaskBlock - 1) / kMaskBlock;
   const bool ext = window > 0 || block_mask != nullptr;
-  // Narrow windows (at most 768 visible keys per row) run on 4-wave
-  // workgroups of 128 rows with 32-key tiles, two per compute unit (three at
-  // head width 64), so one workgroup's loads, item start and output stores
-  // overlap another's arithmetic; such a window moves more bytes per FLOP than the MFMAs need.
-  // Wider windows and block masks alone keep the 8-wave, 64-key walk.
-  const long long span = causal ? (long long)window + 1 : 2LL * window;
-  if (window > 0 && span <= 768) {
+  // Windows and block masks run on 4-wave workgroups of 128 rows (two 64-row
+  // mask blocks) with 32-key tiles, three per compute unit, so one
+  // workgroup's loads, item start and output stores overlap the others'
+  // arithmetic, and a mask block's kept tiles are walked with fewer idle
+  // waves than a 256-row workgroup's four blocks would leave.
+  if (ext) {
     static_assert(kMaskBlock % 32 == 0, "mask blocks hold whole 32-key tiles");
     if (D == 128) return causal ? launch_one<128, 4, 32, true, true>(a, n_cu, stream) : launch_one<128, 4, 32, false, true>(a, n_cu, stream);
     return causal ? launch_one<64, 4, 32, true, true>(a, n_cu, stream) : launch_one<64, 4, 32, false, true>(a, n_cu, stream);
-  }
-  if (ext) {
-    if (D == 128) return causal ? launch_one<128, 8, 64, true, true>(a, n_cu, stream) : launch_one<128, 8, 64, false, true>(a, n_cu, stream);
-    return causal ? launch_one<64, 8, 64, true, true>(a, n_cu, stream) : launch_one<64, 8, 64, false, true>(a, n_cu, stream);
   }
   if (D == 128) return causal ? launch_one<128, 8, 64, true, false>(a, n_cu, stream) : launch_one<128, 8, 64, false, false>(a, n_cu, stream);
   return causal ? launch_one<64, 8, 64, true, false>(a, n_cu, stream) : launch_one<64, 8, 64, false, false>(a, n_cu, stream);
