@@ -302,13 +302,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
             lo = pos - a.window;
           }
         }
+        // Score i of key block kb sits at key b + p_i, b = kv0 + 32*kb + 4*hi,
+        // p_i = 8*(i>>2) + (i&3) <= 27. One bit mask per block marks the
+        // visible offsets lo-b .. lim-b; each score then costs a sign-extended
+        // one-bit extract and a bitfield select against -inf.
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb) {
+          const int b = kv0 + kb * 32 + 4 * hi;
+          const int up = min(max(lim - b, -1), 30) + 1;
+          const int dn = min(max(lo - b, 0), 31);
+          const uint32_t vis = ((1u << up) - 1u) & (~0u << dn);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int j = kv0 + kb * 32 + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (j > lim || j < lo) s[kb][i] = -INFINITY;
+            const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)vis, 8 * (i >> 2) + (i & 3), 1);
+            s[kb][i] = __uint_as_float((__float_as_uint(s[kb][i]) & keep) | (~keep & 0xff800000u));
           }
+        }
       }
       float mx = -INFINITY;
 #pragma unroll
