@@ -37,18 +37,18 @@ MHA_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip", "tiled_attention_
 MLA_SOURCES = ("tiled_attention_12_amd/csrc/mla_decode.hip", "tiled_attention_12_amd/csrc/device_common.h")
 TRAFFIC = {
     "mha_prefill_bf16": {"sources": MHA_SOURCES,
-                         "sources_sha256": "41d12a59ee22277f05efd699b5678701cfa6c3da8716d6423c8f7f686e4f25d8",
-                         "fetch_kib": 82118.4, "write_kib": 33296.8},
+                         "sources_sha256": "447addbddea21886490c00808cc8fcb4eeb20ed1a3ae1b269c82d1b9dbb25ed1",
+                         "fetch_kib": 82118.9, "write_kib": 33298.0},
     "mha_long_causal_bf16": {"sources": MHA_SOURCES,
-                             "sources_sha256": "41d12a59ee22277f05efd699b5678701cfa6c3da8716d6423c8f7f686e4f25d8",
-                             "fetch_kib": 811303.1, "write_kib": 133122.1},
+                             "sources_sha256": "447addbddea21886490c00808cc8fcb4eeb20ed1a3ae1b269c82d1b9dbb25ed1",
+                             "fetch_kib": 832145.2, "write_kib": 133120.8},
     # split + merge kernel of one call
     "mla_decode_bf16": {"sources": MLA_SOURCES,
                         "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
-                        "fetch_kib": 152247.1 + 16498.3, "write_kib": 32896.3 + 8225.4},
+                        "fetch_kib": 152247.1 + 16498.2, "write_kib": 32896.3 + 8227.1},
     "mla_decode_ragged_bf16": {"sources": MLA_SOURCES,
                                "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
-                               "fetch_kib": 667550.4 + 24532.8, "write_kib": 48959.0 + 16449.3},
+                               "fetch_kib": 667543.2 + 24533.9, "write_kib": 48959.0 + 16451.2},
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
