@@ -116,13 +116,15 @@ def test_block_mask(ta, dev, D, causal, density, sq, skv):
     assert_bf16_parity(o, lse, ro, rl, f"block mask d={density} causal={causal} {sq}x{skv}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_block_mask_grouped_heads_and_more_items_than_one_pass(ta, dev, causal):
-    # 4*16 heads of five 256-row query tiles each: more work items than the
-    # chip has compute units, in the XCD order (heads a multiple of 8), 4
-    # query heads per KV head
-    x = inputs.mha_inputs(4, 16, 1100, 1000, 128, seed=985, Hkv=4)
-    mask = inputs.block_mask(4, 16, 1100, 1000, 0.4, seed=986)
+def test_block_mask_grouped_heads_and_more_items_than_one_pass(ta, dev, D, causal):
+    # 4*16 heads of thirteen 128-row query tiles each (the last one ragged):
+    # 832 work items, more than the persistent grid has workgroups (three per
+    # compute unit), in the XCD order (heads a multiple of 8), 4 query heads
+    # per KV head
+    x = inputs.mha_inputs(4, 16, 1600, 1000, D, seed=985 + D, Hkv=4)
+    mask = inputs.block_mask(4, 16, 1600, 1000, 0.4, seed=986)
     o, lse = _run(ta, dev, x, causal, 0.088, mask=mask)
     ro, rl = oracle.attention_masked(*_vals(x, "qkv"), 0.088, causal=causal, block_mask=mask)
     assert np.array_equal(np.isneginf(lse), np.isneginf(rl))
