@@ -104,8 +104,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *
  * A row that sees no key (window, causal rule and mask together) gets O = 0
  * and LSE = -inf. Grouped heads run at the speed of attn_fwd; with a window
- * or a mask the kernel visits only the key tiles some row of a 256-row query
- * tile can see.
+ * or a mask the kernel visits only the 32-key tiles some row of a 128-row
+ * query tile (two 64-row mask blocks) can see.
  */
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                 int B, int H, int Hkv, int Sq, int Skv, int D, int causal, int window,
