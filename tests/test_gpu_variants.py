@@ -83,12 +83,12 @@ def test_wide_sliding_window(ta, dev, D, causal, W):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_narrow_window_more_items_than_workgroup_slots(ta, dev, D, causal):
-    # 4*16 heads of thirteen 128-row query tiles (the last one ragged): 832 work
-    # items, more than the persistent grid has workgroups (three per compute
-    # unit at head width 64, two at 128), in the XCD order. Outputs are
-    # prefilled with NaN so an item that no workgroup wrote fails; every
+    # 4*16 heads of eighteen 128-row query tiles (the last one ragged): 1152
+    # work items, more than the persistent grid has workgroups (four per
+    # compute unit at head width 64, three at 128), in the XCD order. Outputs
+    # are prefilled with NaN so an item that no workgroup wrote fails; every
     # element is checked.
-    x = inputs.mha_inputs(4, 16, 1600, 1600, D, seed=995 + D + int(causal))
+    x = inputs.mha_inputs(4, 16, 2200, 2200, D, seed=995 + D + int(causal))
     q, k, v = (to_dev(x[n], dev) for n in "qkv")
     out = torch.full_like(q, float("nan"))
     lse = torch.full(q.shape[:3], float("nan"), dtype=torch.float32, device=dev)
@@ -119,12 +119,12 @@ def test_block_mask(ta, dev, D, causal, density, sq, skv):
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_block_mask_grouped_heads_and_more_items_than_one_pass(ta, dev, D, causal):
-    # 4*16 heads of thirteen 128-row query tiles each (the last one ragged):
-    # 832 work items, more than the persistent grid has workgroups (three per
-    # compute unit), in the XCD order (heads a multiple of 8), 4 query heads
-    # per KV head
-    x = inputs.mha_inputs(4, 16, 1600, 1000, D, seed=985 + D, Hkv=4)
-    mask = inputs.block_mask(4, 16, 1600, 1000, 0.4, seed=986)
+    # 4*16 heads of eighteen 128-row query tiles each (the last one ragged):
+    # 1152 work items, more than the persistent grid has workgroups (three or
+    # four per compute unit), in the XCD order (heads a multiple of 8), 4
+    # query heads per KV head
+    x = inputs.mha_inputs(4, 16, 2200, 1000, D, seed=985 + D, Hkv=4)
+    mask = inputs.block_mask(4, 16, 2200, 1000, 0.4, seed=986)
     o, lse = _run(ta, dev, x, causal, 0.088, mask=mask)
     ro, rl = oracle.attention_masked(*_vals(x, "qkv"), 0.088, causal=causal, block_mask=mask)
     assert np.array_equal(np.isneginf(lse), np.isneginf(rl))

@@ -33,8 +33,8 @@
 //    2^8 (in base-2 units), so the O rescale runs on few tiles; every
 //    exponential stays <= 2^8 and the result is unchanged (both O and l are
 //    taken relative to the same m).
-//  * Persistent grid: one workgroup per compute unit (three for the 4-wave
-//    window/mask launch) loops over work items (one NW*32-row query tile of
+//  * Persistent grid: one workgroup per compute unit (three or four for the
+//    4-wave window/mask launch) loops over work items (one NW*32-row query tile of
 //    one (batch, head) each). The hardware hands
 //    workgroup i to XCD i % 8 and item i runs on XCD i % 8 too: all query
 //    tiles of a (batch, head) go to one XCD so its K/V stays in that XCD's
@@ -78,11 +78,11 @@ struct MhaArgs {
 // wave's 32 rows lie inside one query block).
 constexpr int kMaskBlock = 64;
 
-// Waves per SIMD: three for the 4-wave window/mask walk (three workgroups per
-// compute unit, within the 168 registers that leaves each wave), two for the
-// others.
+// Waves per SIMD: for the 4-wave window/mask walk four at head width 64 and
+// three at 128 (that many workgroups per compute unit, within the 128 or 168
+// registers it leaves each wave), two for the others.
 template <int D, int NW, bool EXT>
-constexpr int kWavesPerSimd = (EXT && NW == 4) ? 3 : 2;
+constexpr int kWavesPerSimd = (EXT && NW == 4) ? (D == 64 ? 4 : 3) : 2;
 
 // The 4-wave walk at head width 128 takes the lane id through an opaque copy
 // per work item, so its lane-dependent addresses are recomputed per item
@@ -746,7 +746,7 @@ hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void
   a.nkb = (Skv + kMaskBlock - 1) / kMaskBlock;
   const bool ext = window > 0 || block_mask != nullptr;
   // Windows and block masks run on 4-wave workgroups of 128 rows (two 64-row
-  // mask blocks) with 32-key tiles, three per compute unit, so one
+  // mask blocks) with 32-key tiles, three or four per compute unit, so one
   // workgroup's loads, item start and output stores overlap the others'
   // arithmetic, and a mask block's kept tiles are walked with fewer idle
   // waves than a 256-row workgroup's four blocks would leave.
