@@ -37,18 +37,18 @@ MHA_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip", "tiled_attention_
 MLA_SOURCES = ("tiled_attention_12_amd/csrc/mla_decode.hip", "tiled_attention_12_amd/csrc/device_common.h")
 TRAFFIC = {
     "mha_prefill_bf16": {"sources": MHA_SOURCES,
-                         "sources_sha256": "447addbddea21886490c00808cc8fcb4eeb20ed1a3ae1b269c82d1b9dbb25ed1",
-                         "fetch_kib": 82118.9, "write_kib": 33298.0},
+                         "sources_sha256": "ec8f28592862a6964a53373dec7feeecac8e5c1e748416b146cea12530c10e84",
+                         "fetch_kib": 82118.8, "write_kib": 33355.8},
     "mha_long_causal_bf16": {"sources": MHA_SOURCES,
-                             "sources_sha256": "447addbddea21886490c00808cc8fcb4eeb20ed1a3ae1b269c82d1b9dbb25ed1",
-                             "fetch_kib": 832145.2, "write_kib": 133120.8},
+                             "sources_sha256": "ec8f28592862a6964a53373dec7feeecac8e5c1e748416b146cea12530c10e84",
+                             "fetch_kib": 815287.1, "write_kib": 133120.8},
     # split + merge kernel of one call
     "mla_decode_bf16": {"sources": MLA_SOURCES,
                         "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
-                        "fetch_kib": 152247.1 + 16498.2, "write_kib": 32896.3 + 8227.1},
+                        "fetch_kib": 152247.1 + 16498.2, "write_kib": 32896.3 + 8225.8},
     "mla_decode_ragged_bf16": {"sources": MLA_SOURCES,
                                "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
-                               "fetch_kib": 667543.2 + 24533.9, "write_kib": 48959.0 + 16451.2},
+                               "fetch_kib": 667567.9 + 24533.1, "write_kib": 48959.0 + 16449.4},
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
