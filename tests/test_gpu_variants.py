@@ -142,6 +142,32 @@ def test_all_variants_together(ta, dev, causal, W):
     assert_bf16_parity(o, lse, ro, rl, f"gqa+window W={W}+mask causal={causal}")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("jump", [24.0, 200.0, -200.0])
+def test_window_and_mask_score_jumps(ta, dev, D, jump):
+    # the window/mask walk takes the exact step on every tile (tile max,
+    # raise past the threshold, O rescale): from key 640 on one query/key
+    # dimension adds `jump` base-2 units to every score, under a window and
+    # under a block mask
+    B, H, S = 1, 2, 1000
+    x = inputs.mha_inputs(B, H, S, S, D, seed=46)
+    q = inputs.stored_values(x["q"]).copy()
+    k = inputs.stored_values(x["k"]).copy()
+    scale = float(np.float32(D ** -0.5))
+    q[..., 0] = 1.0
+    k[..., 0] = 0.0
+    k[..., 640:, 0] = jump * np.log(2.0) / scale
+    y = dict(x, q=inputs.f32_to_bf16_bits(q), k=inputs.f32_to_bf16_bits(k))
+    mask = inputs.block_mask(B, H, S, S, 0.7, seed=47)
+    for causal in (False, True):
+        for window, m in ((300, None), (0, mask)):
+            o, lse = _run(ta, dev, y, causal, scale, window=window, mask=m)
+            ro, rl = oracle.attention_masked(*_vals(y, "qkv"), scale, causal=causal, window=window,
+                                             block_mask=m)
+            assert np.array_equal(np.isneginf(lse), np.isneginf(rl))
+            assert_bf16_parity(o, lse, ro, rl, f"jump {jump} D={D} causal={causal} W={window} mask={m is not None}")
+
+
 def test_masked_out_everything(ta, dev):
     x = inputs.mha_inputs(1, 2, 130, 200, 64, seed=992)
     mask = np.zeros((1, 2, 3, 4), np.uint8)
