@@ -8,8 +8,8 @@
 // FlashMLA" (section 3.1) does. The K/V tile loop is software pipelined over
 // LDS stages (section 2.2 there).
 //
-// gfx950 mapping (one workgroup = NW waves = NW*32 query rows, two waves per
-// SIMD):
+// gfx950 mapping (one workgroup = NW waves = NW*32 query rows; the dense
+// launch has 8 waves, two per SIMD):
 //  * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16. Q^T is the B operand and is
 //    loaded once into registers; K comes from LDS as the A operand. With S
 //    transposed, lane l owns query column l%32 and 16 of the 32 keys of each
@@ -27,19 +27,27 @@
 //  * Each wave runs one tile behind itself: after barrier t it forms the
 //    scores of tile t on the MFMAs while the VALU exponentiates the scores of
 //    tile t-1 (instruction groups interleaved with sched_group_barrier), then
-//    accumulates P*V of tile t-1. Tiles that need masks (causal diagonal,
-//    ragged tail) run unpipelined afterwards.
-//  * The running max is only raised when a new score exceeds it by more than
-//    2^8 (in base-2 units), so the O rescale runs on few tiles; every
-//    exponential stays <= 2^8 and the result is unchanged (both O and l are
-//    taken relative to the same m).
-//  * Persistent grid: one workgroup per compute unit (three or four for the
-//    4-wave window/mask launch) loops over work items (one NW*32-row query tile of
-//    one (batch, head) each). The hardware hands
-//    workgroup i to XCD i % 8 and item i runs on XCD i % 8 too: all query
-//    tiles of a (batch, head) go to one XCD so its K/V stays in that XCD's
-//    L2. Causal items are taken longest first, and each workgroup's passes
-//    alternate direction so long and short tiles pair up.
+//    accumulates P*V of tile t-1. These tiles are exponentiated against tile
+//    0's max without forming their own maxima; after the item each wave
+//    checks l and O for overflow and, if one is found, writes its rows again
+//    with an exact fp32 online softmax. Tiles that need masks (causal
+//    diagonal, ragged tail) run unpipelined afterwards with the exact step.
+//  * Exact step: the running max is only raised when a new score exceeds it
+//    by more than 2^8 (in base-2 units), so the O rescale runs on few tiles;
+//    every exponential stays <= 2^8 and the result is unchanged (both O and l
+//    are taken relative to the same m). Masks take one bit mask of the
+//    visible keys per 32-key block, then a one-bit extract and a bitfield
+//    select per score.
+//  * Windows and block masks run a separate walk: 4-wave workgroups of 128
+//    rows (two 64-row mask blocks), 32-key tiles, three or four workgroups
+//    per compute unit, visiting only the tiles some row sees and the mask
+//    keeps, every visited tile through the exact step.
+//  * Persistent grid: as many workgroups as fit on the compute units loop
+//    over work items (one NW*32-row query tile of one (batch, head) each).
+//    The hardware hands workgroup i to XCD i % 8 and item i runs on XCD i % 8
+//    too: all query tiles of a (batch, head) go to one XCD so its K/V stays
+//    in that XCD's L2. Causal items are taken longest first, and each
+//    workgroup's passes alternate direction so long and short tiles pair up.
 #include "device_common.h"
 #include "launch.h"
 
