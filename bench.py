@@ -37,10 +37,10 @@ MHA_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip", "tiled_attention_
 MLA_SOURCES = ("tiled_attention_12_amd/csrc/mla_decode.hip", "tiled_attention_12_amd/csrc/device_common.h")
 TRAFFIC = {
     "mha_prefill_bf16": {"sources": MHA_SOURCES,
-                         "sources_sha256": "808f59049f524e2260d14754c6b77694a961d0ea13d52cd5c4bc98075517f083",
+                         "sources_sha256": "e1d3f3c5411994f0a77b97d0e538655cdccb07c1071fdbaf9a4cfa4dab574078",
                          "fetch_kib": 82118.8, "write_kib": 33355.8},
     "mha_long_causal_bf16": {"sources": MHA_SOURCES,
-                             "sources_sha256": "808f59049f524e2260d14754c6b77694a961d0ea13d52cd5c4bc98075517f083",
+                             "sources_sha256": "e1d3f3c5411994f0a77b97d0e538655cdccb07c1071fdbaf9a4cfa4dab574078",
                              "fetch_kib": 815287.1, "write_kib": 133120.8},
     # split + merge kernel of one call
     "mla_decode_bf16": {"sources": MLA_SOURCES,

@@ -13,7 +13,7 @@ namespace tattn {
 int g_stub_launches = 0;
 
 hipError_t launch_mha_fwd_bf16(const void*, const void*, const void*, void*, float*, int, int, int, int, int,
-                               int, bool, int, const uint8_t*, float, int, hipStream_t) {
+                               int, bool, int, const uint8_t*, float, int, int, hipStream_t) {
   ++g_stub_launches;
   return hipSuccess;
 }

@@ -36,6 +36,15 @@ def _vals(x, names):
     return [inputs.stored_values(x[n]) for n in names]
 
 
+@pytest.fixture(params=[4, 8], ids=["waves4", "waves8"])
+def dense_waves(request, monkeypatch):
+    """Forces the dense prefill's workgroup shape (4 waves x 128 rows, two per
+    CU, or 8 waves x 256 rows); unset, the launcher picks it from the launch
+    size, and small test shapes would only reach the 4-wave one."""
+    monkeypatch.setenv("TATTN_MHA_WAVES", str(request.param))
+    return request.param
+
+
 def _run_mha(ta, dev, x, causal, scale, fp32=False):
     q, k, v = (to_dev(x[n], dev) for n in "qkv")
     fn = ta.attn_fwd_f32 if fp32 else ta.attn_fwd
@@ -66,7 +75,7 @@ SHAPES = [(1, 1), (7, 7), (63, 63), (64, 64), (65, 65), (127, 129), (129, 127), 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("sq,skv", SHAPES)
-def test_bf16_shapes(ta, dev, D, causal, sq, skv):
+def test_bf16_shapes(ta, dev, D, causal, sq, skv, dense_waves):
     x = inputs.mha_inputs(2, 3, sq, skv, D, seed=7 * sq + skv + D + int(causal))
     scale = float(np.float32(D ** -0.5))
     o, lse = _run_mha(ta, dev, x, causal, scale)
@@ -74,7 +83,7 @@ def test_bf16_shapes(ta, dev, D, causal, sq, skv):
     assert_bf16_parity(o, lse, ro, rl, f"bf16 D={D} causal={causal} {sq}x{skv}")
 
 
-def test_bf16_empty_keys_and_fully_masked_rows(ta, dev):
+def test_bf16_empty_keys_and_fully_masked_rows(ta, dev, dense_waves):
     x = inputs.mha_inputs(1, 2, 40, 0, 128, seed=3)
     q = to_dev(x["q"], dev)
     kv = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device=dev)
@@ -105,7 +114,7 @@ def test_bf16_single_and_identical_keys(ta, dev):
     assert np.abs(lse - rl).max() <= 1e-3
 
 
-def test_bf16_causal_row0_and_future_keys(ta, dev):
+def test_bf16_causal_row0_and_future_keys(ta, dev, dense_waves):
     x = inputs.mha_inputs(2, 2, 333, 333, 128, seed=11)
     o1, l1 = _run_mha(ta, dev, x, True, 0.09)
     v = inputs.stored_values(x["v"]).astype(np.float64)
@@ -155,6 +164,44 @@ def test_bf16_deterministic(ta, dev):
     a = _run_mha(ta, dev, x, True, 0.088)
     b = _run_mha(ta, dev, x, True, 0.088)
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_shape_choice_follows_the_launch_size(ta, dev, causal, monkeypatch):
+    # unforced, a launch with few 256-row items runs the 4-wave shape and a
+    # launch with at least one item per CU the 8-wave shape: the automatic
+    # result is bitwise the forced one (both shapes compute each row alike,
+    # but which tiles a shape masks can change the rounding, so the two shapes
+    # are compared with the oracle, not with each other)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    D = 128
+    cases = [(1, 2, 700, 4)]  # 2 * 3 items of 256 rows
+    big_h = -(-cus // 4)  # 4 items of 256 rows per head: at least one item per CU
+    cases.append((1, big_h, 1024, 8))
+    for B, H, S, expect in cases:
+        x = inputs.mha_inputs(B, H, S, S, D, seed=90 + H)
+        monkeypatch.delenv("TATTN_MHA_WAVES", raising=False)
+        auto = _run_mha(ta, dev, x, causal, 0.088)
+        monkeypatch.setenv("TATTN_MHA_WAVES", str(expect))
+        forced = _run_mha(ta, dev, x, causal, 0.088)
+        assert np.array_equal(auto[0], forced[0]) and np.array_equal(auto[1], forced[1]), (B, H, S, expect)
+    monkeypatch.delenv("TATTN_MHA_WAVES")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_shapes_with_more_items_than_workgroup_slots(ta, dev, causal, dense_waves):
+    # 4 x 16 heads of 1100 rows: 576 items of 128 rows (more than two per CU
+    # at 256 CUs) or 320 of 256; outputs start as NaN so a skipped or
+    # mis-mapped item fails, and every element is checked
+    B, H, S, D = 4, 16, 1100, 128
+    x = inputs.mha_inputs(B, H, S, S, D, seed=93 + int(causal))
+    q, k, v = (to_dev(x[n], dev) for n in "qkv")
+    o = torch.full((B, H, S, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=dev)
+    ta.attn_fwd(q, k, v, causal=causal, scale=0.088, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(*_vals(x, "qkv"), 0.088, causal=causal)
+    assert_bf16_parity(to_np(o), to_np(lse), ro, rl, f"{dense_waves} waves, {B}x{H}x{S} causal={causal}")
 
 
 # ------------------------------------------------------------------ MLA decode
@@ -376,7 +423,7 @@ def test_more_items_than_compute_units_without_xcd_order(ta, dev, causal):
 
 # ------------------------------------------------------------------ running-max raises
 
-def test_bf16_running_max_rises_across_tiles(ta, dev):
+def test_bf16_running_max_rises_across_tiles(ta, dev, dense_waves):
     # one query/key dimension carries a score ramp along the key index (about
     # 9 base-2 units per 64 keys), so the running max is raised again and
     # again after the first tile and the accumulator rescale runs; a rescale
@@ -398,7 +445,7 @@ def test_bf16_running_max_rises_across_tiles(ta, dev):
 
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("jump", [24.0, 200.0, -200.0])
-def test_running_max_jumps_inside_the_sequence(ta, dev, jump, D):
+def test_running_max_jumps_inside_the_sequence(ta, dev, jump, D, dense_waves):
     # from key 640 on, one query/key dimension adds `jump` base-2 units to
     # every score: exponentials taken against the running max of the keys
     # before would reach 2^24 or overflow to inf (or, for a drop, underflow
@@ -418,7 +465,7 @@ def test_running_max_jumps_inside_the_sequence(ta, dev, jump, D):
         assert_bf16_parity(o, lse, ro, rl, f"score jump {jump} D={D} causal={causal}")
 
 
-def test_grouped_heads_score_jump(ta, dev):
+def test_grouped_heads_score_jump(ta, dev, dense_waves):
     # the grouped-KV path shares the dense kernel's overflow check and exact
     # recompute: a 200-unit jump in the keys of one KV head
     B, H, Hkv, S, D = 1, 4, 2, 700, 128

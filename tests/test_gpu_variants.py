@@ -31,6 +31,14 @@ def ta(lib_path):
     return ta
 
 
+@pytest.fixture(params=[4, 8], ids=["waves4", "waves8"])
+def dense_waves(request, monkeypatch):
+    """Forces the dense prefill's workgroup shape (grouped heads without a
+    window or mask take the dense path)."""
+    monkeypatch.setenv("TATTN_MHA_WAVES", str(request.param))
+    return request.param
+
+
 def _vals(x, names):
     return [inputs.stored_values(x[n]) for n in names]
 
@@ -47,7 +55,7 @@ def _run(ta, dev, x, causal, scale, window=0, mask=None):
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Hkv", [1, 2, 4, 8])
 @pytest.mark.parametrize("sq,skv", [(130, 130), (65, 300), (300, 65)])
-def test_grouped_kv_heads(ta, dev, D, causal, Hkv, sq, skv):
+def test_grouped_kv_heads(ta, dev, D, causal, Hkv, sq, skv, dense_waves):
     x = inputs.mha_inputs(2, 8, sq, skv, D, seed=900 + Hkv + sq + D, Hkv=Hkv)
     scale = float(np.float32(D ** -0.5))
     o, lse = _run(ta, dev, x, causal, scale)

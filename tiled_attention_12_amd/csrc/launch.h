@@ -10,10 +10,13 @@ namespace tattn {
 
 // K and V hold Hkv heads (H a multiple of Hkv); window 0 means no window;
 // block_mask is null or a device [B, H, ceil(Sq/64), ceil(Skv/64)] byte mask;
-// n_cu is the device's compute-unit count (the persistent grid size).
+// n_cu is the device's compute-unit count (the persistent grid size);
+// dense_waves 4 or 8 forces the workgroup shape of the dense path, anything
+// else leaves the choice to the launch size.
 hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int Hkv, int Sq, int Skv, int D, bool causal, int window,
-                               const uint8_t* block_mask, float scale, int n_cu, hipStream_t stream);
+                               const uint8_t* block_mask, float scale, int n_cu, int dense_waves,
+                               hipStream_t stream);
 
 hipError_t launch_mha_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                               int B, int H, int Sq, int Skv, int D, bool causal, float scale,

@@ -38,6 +38,13 @@
 //    are taken relative to the same m). Masks take one bit mask of the
 //    visible keys per 32-key block, then a one-bit extract and a bitfield
 //    select per score.
+//  * Small dense launches (fewer 256-row items than compute units; without a
+//    mask, at most half as many) run the same steps in 4-wave workgroups of
+//    128 rows, two per compute unit: half-height items shorten the longest
+//    item and spread over more compute units. Their ring holds two K and two
+//    V stages (64 KB): the pipelined steps refill K of tile t+1 and V of tile
+//    t at barrier t, so V is loaded one step after its K, while its P*V is
+//    still a step away.
 //  * Windows and block masks run a separate walk: 4-wave workgroups of 128
 //    rows (two 64-row mask blocks), 32-key tiles, three or four workgroups
 //    per compute unit, visiting only the tiles some row sees and the mask
@@ -116,8 +123,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
   static_assert(NSTAGE * TILE <= 65536, "LDS offsets must fit the 16-bit instruction offset");
   // Tile t+PF is loaded while tile t is scored and tile t-1 accumulated, so
   // the ring needs PF + 2 stages.
-  constexpr int PF = NSTAGE - 2;
+  // The dense 4-wave shape refills K and V one step apart (K of tile t+1 and
+  // V of tile t at barrier t), so two stages of each suffice.
+  constexpr bool SKV = !EXT && NW == 4;
+  constexpr int PF = SKV ? 1 : NSTAGE - 2;
   static_assert(PF == 1 || PF == 2, "prefetch distance 1 or 2");
+  static_assert(!SKV || NSTAGE == 2, "split refills: two K and two V stages");
   constexpr int UN = NSTAGE % 2 == 0 ? NSTAGE : 2 * NSTAGE;  // unroll: stages x score sets
   constexpr float TAU = 8.0f;
 
@@ -191,9 +202,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
       }
     }
 
-    // Tile t -> stage ST: wave loads n cover chunk slots (n*NW + wave)*64 + lane.
-    auto issue = [&](int t, auto STc) {
+    // Tile t -> stage ST: wave loads n cover chunk slots (n*NW + wave)*64 + lane;
+    // WH selects the K (1) and/or V (2) half.
+    auto issue_kv = [&](int t, auto STc, auto WHc) {
       constexpr int ST = decltype(STc)::value;
+      constexpr int WH = decltype(WHc)::value;
       const int lim = Skv - 1 - t * BC;  // >= 0: tile t has a visible key
       const char* kt = kp + (size_t)t * BC * RS;
       const char* vt = vp + (size_t)t * BC * RS;
@@ -203,12 +216,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
         const int row = slot / CPR;
         const uint32_t off = (uint32_t)(min(row, lim) * RS + 16 * swz<CPR>(row, slot % CPR));
         const uint32_t dst = smem0 + ST * TILE + (n * NW + wave) * 1024;
-        load_lds16_sbase(kt, off, dst);
-        load_lds16_sbase(vt, off, dst + VREG);
+        if constexpr ((WH & 1) != 0) load_lds16_sbase(kt, off, dst);
+        if constexpr ((WH & 2) != 0) load_lds16_sbase(vt, off, dst + VREG);
       }
     };
+    using OnlyK = std::integral_constant<int, 1>;
+    using OnlyV = std::integral_constant<int, 2>;
+    auto issue = [&](int t, auto STc) { issue_kv(t, STc, std::integral_constant<int, 3>{}); };
 
-    if constexpr (!EXT) {
+    // Tiles 0 .. t_main-1 need no mask (the pipelined part of the dense path).
+    auto first_masked_tile = [&]() {
+      int t = Skv / BC;
+      if (CAUSAL) t = min(t, max(0, (q0 + Skv - Sq + 1) / BC));
+      return min(t, nt);
+    };
+    if constexpr (SKV) {
+      // V of tile 0 follows at its barrier, unless no tile is pipelined
+      if (0 < nt) {
+        if (first_masked_tile() > 0) issue_kv(0, std::integral_constant<int, 0>{}, OnlyK{});
+        else issue(0, std::integral_constant<int, 0>{});
+      }
+    } else if constexpr (!EXT) {
       static_for<PF>([&](auto Ic) {
         if (decltype(Ic)::value < nt) issue(decltype(Ic)::value, Ic);
       });
@@ -468,16 +496,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
       // step (tile max, threshold raise, O rescale) on every tile.
       f32x16 sb[2][KB];
       f32x16 (&s_cur)[KB] = sb[0];
-      int t_plain = Skv / BC;
-      if (CAUSAL) t_plain = min(t_plain, max(0, (q0 + Skv - Sq + 1) / BC));
-      t_plain = min(t_plain, nt);
-      // pipelined tiles: 0 .. t_main-1 (every tile that needs no mask)
-      const int t_main = t_plain;
+      const int t_main = first_masked_tile();
       if (t_main > 0) {
         wait_tile(0);
         wait_lgkmcnt0();
         barrier();
-        if (PF < nt) issue(PF, std::integral_constant<int, PF % NSTAGE>{});
+        if constexpr (SKV) {
+          if (1 < nt) issue_kv(1, std::integral_constant<int, 1>{}, OnlyK{});
+          issue_kv(0, std::integral_constant<int, 0>{}, OnlyV{});
+        } else if (PF < nt) {
+          issue(PF, std::integral_constant<int, PF % NSTAGE>{});
+        }
         m1(std::integral_constant<int, 0>{}, sb[0]);
         // the reference: tile 0's max (no key of a pipelined tile is masked,
         // so it is finite for every row)
@@ -492,7 +521,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
             wait_tile(t);
             wait_lgkmcnt0();
             barrier();
-            if (t + PF < nt) issue(t + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
+            if constexpr (SKV) {
+              if (t + 1 < nt) issue_kv(t + 1, std::integral_constant<int, (ST + 1) % NSTAGE>{}, OnlyK{});
+              issue_kv(t, std::integral_constant<int, ST>{}, OnlyV{});
+            } else if (t + PF < nt) {
+              issue(t + PF, std::integral_constant<int, (ST + PF) % NSTAGE>{});
+            }
             bf16x8 pf[KB][2];
             vexp(sb[BP], pf);
             m1(std::integral_constant<int, ST>{}, sb[BN]);
@@ -513,6 +547,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
               __builtin_amdgcn_sched_group_barrier(0x008, DB, 0);
             });
           });
+        }
+        if constexpr (SKV) {
+          // V of tile t_main - 1 was issued at that tile's barrier; from here
+          // on K and V of a tile are loaded together, so V of tile t_main
+          // follows now
+          wait_vmcnt<0>();
+          wait_lgkmcnt0();
+          barrier();
+          if (t_main < nt) {
+            if (t_main % 2 == 0) issue_kv(t_main, std::integral_constant<int, 0>{}, OnlyV{});
+            else issue_kv(t_main, std::integral_constant<int, 1>{}, OnlyV{});
+          }
         }
         // tile t_main - 1 still needs its softmax and P*V; its stage and
         // score set follow from its position in the unrolled pass
@@ -706,9 +752,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(kWavesP
 template <int D, int NW, int BC, bool CAUSAL, bool EXT>
 static hipError_t launch_one(const MhaArgs& a, int n_cu, hipStream_t stream) {
   constexpr int BR = NW * 32;
-  constexpr int NSTAGE = TATTN_MHA_STAGES;
-  // the K and V rings, then one flag per wave
-  constexpr size_t lds = 2 * (size_t)NSTAGE * BC * D * 2 + 4 * NW;
+  constexpr int NSTAGE = (!EXT && NW == 4) ? 2 : TATTN_MHA_STAGES;
+  // the K and V rings
+  constexpr size_t lds = 2 * (size_t)NSTAGE * BC * D * 2;
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = mha_fwd_bf16_kernel<D, NW, BC, NSTAGE, CAUSAL, EXT>;
   // Thread-safe one-time opt-in to more than the default dynamic LDS.
@@ -735,7 +781,8 @@ static hipError_t launch_one(const MhaArgs& a, int n_cu, hipStream_t stream) {
 
 hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int H, int Hkv, int Sq, int Skv, int D, bool causal, int window,
-                               const uint8_t* block_mask, float scale, int n_cu, hipStream_t stream) {
+                               const uint8_t* block_mask, float scale, int n_cu, int dense_waves,
+                               hipStream_t stream) {
   MhaArgs a{};
   a.q = (const uint16_t*)q;
   a.k = (const uint16_t*)k;
@@ -762,6 +809,18 @@ hipError_t launch_mha_fwd_bf16(const void* q, const void* k, const void* v, void
     static_assert(kMaskBlock % 32 == 0, "mask blocks hold whole 32-key tiles");
     if (D == 128) return causal ? launch_one<128, 4, 32, true, true>(a, n_cu, stream) : launch_one<128, 4, 32, false, true>(a, n_cu, stream);
     return causal ? launch_one<64, 4, 32, true, true>(a, n_cu, stream) : launch_one<64, 4, 32, false, true>(a, n_cu, stream);
+  }
+  // Dense: 8-wave workgroups of 256 rows, one per CU. When the launch has
+  // fewer 256-row items than CUs, 4-wave workgroups of 128 rows (two per CU)
+  // instead: causally, half-height items halve the longest item; without a
+  // mask only when at most half the CUs would be busy (each 4-wave workgroup
+  // then has its CU to itself; two sharing one are ~16 % slower per row).
+  const long long items8 = (long long)a.n_bh * ((Sq + 255) / 256);
+  bool four = causal ? items8 < n_cu : 2 * items8 <= n_cu;
+  if (dense_waves == 4 || dense_waves == 8) four = dense_waves == 4;
+  if (four) {
+    if (D == 128) return causal ? launch_one<128, 4, 64, true, false>(a, n_cu, stream) : launch_one<128, 4, 64, false, false>(a, n_cu, stream);
+    return causal ? launch_one<64, 4, 64, true, false>(a, n_cu, stream) : launch_one<64, 4, 64, false, false>(a, n_cu, stream);
   }
   if (D == 128) return causal ? launch_one<128, 8, 64, true, false>(a, n_cu, stream) : launch_one<128, 8, 64, false, false>(a, n_cu, stream);
   return causal ? launch_one<64, 8, 64, true, false>(a, n_cu, stream) : launch_one<64, 8, 64, false, false>(a, n_cu, stream);

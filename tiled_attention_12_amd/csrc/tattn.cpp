@@ -116,6 +116,17 @@ Workspace& slot_for(DeviceWorkspaces& d, hipStream_t s) {
   return *lru;
 }
 
+// Workgroup shape of the dense prefill: TATTN_MHA_WAVES = 4 or 8 forces it
+// (a test hook: both shapes must give the same result); otherwise the
+// launcher picks it from the launch size.
+int mha_dense_waves() {
+  if (const char* v = std::getenv("TATTN_MHA_WAVES")) {
+    const long n = std::strtol(v, nullptr, 10);
+    if (n == 4 || n == 8) return (int)n;
+  }
+  return 0;
+}
+
 // Shared validation of the two MHA entry points. Returns TATTN_OK with
 // *nothing = true when there is no work.
 int check_mha(const void* q, const void* k, const void* v, const void* o, const void* lse, int B, int H,
@@ -148,7 +159,7 @@ TATTN_API int attn_fwd(const void* q, const void* k, const void* v, void* o, flo
   int cus = 0;
   if ((st = current_device_cus(&cus)) != TATTN_OK) return st;
   return status_of(tattn::launch_mha_fwd_bf16(q, k, v, o, lse, B, H, H, Sq, Skv, D, causal != 0, 0, nullptr,
-                                              scale, cus, (hipStream_t)stream));
+                                              scale, cus, mha_dense_waves(), (hipStream_t)stream));
 }
 
 TATTN_API int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -164,7 +175,7 @@ TATTN_API int attn_fwd_ex(const void* q, const void* k, const void* v, void* o, 
   int cus = 0;
   if ((st = current_device_cus(&cus)) != TATTN_OK) return st;
   return status_of(tattn::launch_mha_fwd_bf16(q, k, v, o, lse, B, H, Hkv, Sq, Skv, D, causal != 0, window,
-                                              block_mask, scale, cus, (hipStream_t)stream));
+                                              block_mask, scale, cus, mha_dense_waves(), (hipStream_t)stream));
 }
 
 TATTN_API int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B, int H,
