@@ -159,6 +159,21 @@ def _mha_workload(ta, dev, name):
     return w, _copies(x, dev)
 
 
+def _variant_workload(ta, dev, name):
+    """Grouped-head, window or block-mask workload: (spec, input copies,
+    window, mask as numpy or None, mask on the device or None)."""
+    from tiled_attention_12_amd import inputs
+    from tiled_attention_12_amd.workloads import WORKLOADS
+    wv = WORKLOADS[name]
+    xv = inputs.mha_inputs(wv["B"], wv["H"], wv["Sq"], wv["Skv"], wv["D"], seed=wv["seed"],
+                           sigma=wv["sigma"], Hkv=wv.get("Hkv"))
+    mask_np = mask_dev = None
+    if "density" in wv:
+        mask_np = inputs.block_mask(wv["B"], wv["H"], wv["Sq"], wv["Skv"], wv["density"], seed=wv["seed"] + 100)
+        mask_dev = _to_dev(mask_np, dev)
+    return wv, _copies(xv, dev), wv.get("window", 0), mask_np, mask_dev
+
+
 def _mla_workload(ta, dev, name):
     from tiled_attention_12_amd import inputs
     from tiled_attention_12_amd.workloads import WORKLOADS
@@ -298,11 +313,24 @@ def _cpu_baselines(budget_s=5.0):
     return out
 
 
+# profiling names of the grouped-head, window and block-mask workloads:
+# name -> (workload, causal)
+VARIANT_ONLY = {"mha_gqa_bf16": ("mha_gqa_bf16", False), "mha_gqa_bf16_causal": ("mha_gqa_bf16", True),
+                "mha_window_bf16": ("mha_window_bf16", True),
+                "mha_blocksparse_bf16": ("mha_blocksparse_bf16", False)}
+
+
 def _profile_only(args, ta, dev):
     """Run args.steps launches of one workload (after args.warmup) and print its mean time."""
     import torch
     name = args.only
-    if name.startswith("mha"):
+    if name in VARIANT_ONLY:
+        base, causal = VARIANT_ONLY[name]
+        w, sets, window, _, mask_dev = _variant_workload(ta, dev, base)
+        o, l = ta.attn_fwd_ex(sets[0]["q"], sets[0]["k"], sets[0]["v"], scale=w["scale"])
+        fn = lambda s: ta.attn_fwd_ex(s["q"], s["k"], s["v"], causal=causal, scale=w["scale"], window=window,
+                                      block_mask=mask_dev, out=o, lse=l)
+    elif name.startswith("mha"):
         causal = name != "mha_prefill_bf16"
         w, sets = _mha_workload(ta, dev, name.replace("_causal", "") if name == "mha_prefill_bf16_causal" else name)
         o, l = ta.attn_fwd(sets[0]["q"], sets[0]["k"], sets[0]["v"], causal=causal, scale=w["scale"])
@@ -330,7 +358,8 @@ def main():
                     help="only the headline prefill workload (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["mha_prefill_bf16", "mha_prefill_bf16_causal", "mha_long_causal_bf16",
-                                       "mla_decode_bf16", "mla_decode_ragged_bf16", "ssd_scan_bf16"],
+                                       "mla_decode_bf16", "mla_decode_ragged_bf16", "ssd_scan_bf16"]
+                                      + list(VARIANT_ONLY),
                     help="profiling mode: run --steps launches of one workload, print its timing only")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="profiling mode: first run one device-to-device copy of this many MiB "
@@ -443,19 +472,10 @@ def main():
                                   "mha_fwd_bf16_kernel<128, 8, 64, 3, true, false> (causal)", f3)}
         del sets3, o3, l3
 
-        from tiled_attention_12_amd import inputs
-        from tiled_attention_12_amd.workloads import WORKLOADS, visible_pairs
+        from tiled_attention_12_amd.workloads import visible_pairs
         for name in ("mha_gqa_bf16", "mha_window_bf16", "mha_blocksparse_bf16"):
             _log(f"bench: {name}")
-            wv = WORKLOADS[name]
-            xv = inputs.mha_inputs(wv["B"], wv["H"], wv["Sq"], wv["Skv"], wv["D"], seed=wv["seed"],
-                                   sigma=wv["sigma"], Hkv=wv.get("Hkv"))
-            setsv = _copies(xv, dev)
-            window = wv.get("window", 0)
-            mask_np = mask_dev = None
-            if "density" in wv:
-                mask_np = inputs.block_mask(wv["B"], wv["H"], wv["Sq"], wv["Skv"], wv["density"], seed=wv["seed"] + 100)
-                mask_dev = _to_dev(mask_np, dev)
+            wv, setsv, window, mask_np, mask_dev = _variant_workload(ta, dev, name)
             ov, lv = ta.attn_fwd_ex(setsv[0]["q"], setsv[0]["k"], setsv[0]["v"], scale=wv["scale"])
             for causal in wv["causal"]:
                 fn = (lambda s, c=causal: ta.attn_fwd_ex(s["q"], s["k"], s["v"], causal=c, scale=wv["scale"],
