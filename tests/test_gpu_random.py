@@ -1,0 +1,135 @@
+"""Seeded random configurations of the prefill and decode entry points,
+every element compared with the float64 oracle (needs gfx950).
+
+Each case draws its own shape and options from a fixed seed: batch, query and
+KV head counts (grouped or not), ragged query and key lengths, head width,
+causal mask, sliding window, block-mask density, input magnitude, scale and
+the dense prefill's workgroup shape (automatic or forced), or, for the
+decode, the batch count, head count and per-batch key counts (empty batches
+included). Outputs start as NaN so an unwritten element fails.
+
+Gates. Inputs drawn with standard deviation sigma (a power of two) give
+outputs sigma times as large, so O is compared after dividing both sides by
+sigma (exact). The mean, LSE and relative-L2 gates are those of the other
+edge tests. The per-element gate is the error bound of a bf16-P kernel:
+with P rounded to bf16 for the P*V product (8 significant bits: relative
+error <= 2^-8 per term) and the row sum l kept in fp32,
+|dO| <= 2^-8 * sum_j p_j |v_j| / l <= 2^-8 * max |v_j|, plus the half-ulp of
+rounding O itself to bf16, plus the fp32 accumulation of the P*V sums (at
+most Skv 2^-24 max|v|). Very peaked rows (large sigma and scale) come close
+to it: the steps exponentiate against a running max that may sit below the
+row's true max (tile 0's max on the dense path, a max raised only by more
+than 2^8 on the exact step), so even a row's dominant term 2^d (0 <= d <= 8)
+is rounded, where with the exact row max it would be 1. For unit-variance
+inputs (max|v| ~ 4.5) the bound is ~0.018 plus the half-ulp; the errors
+measured there stay under 1e-2, and the configuration tests hold them to it.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.helpers import (BF16_MAX_ABS_LSE, BF16_REL_L2_O, assert_bf16_parity, bf16_half_ulp,
+                           bf16_mean_o_bound, parity_stats, to_dev, to_np)
+from tiled_attention_12_amd import inputs
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no ROCm GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def ta(lib_path):
+    import tiled_attention_12_amd as ta
+    return ta
+
+
+def _prefill_case(i):
+    rng = np.random.default_rng(5000 + i)
+    hkv = int(rng.choice([1, 2, 4]))
+    c = {"B": int(rng.integers(1, 4)), "Hkv": hkv, "H": hkv * int(rng.choice([1, 2, 4])),
+         "Sq": int(rng.integers(1, 520)), "Skv": int(rng.integers(1, 520)), "D": int(rng.choice([64, 128])),
+         "causal": bool(rng.integers(0, 2)),
+         "window": int(rng.integers(1, 400)) if rng.random() < 0.35 else 0,
+         "density": float(rng.uniform(0.15, 0.9)) if rng.random() < 0.3 else None,
+         "sigma": float(rng.choice([0.5, 1.0, 2.0])),
+         "waves": str(rng.choice(["auto", "4", "8"]))}
+    c["scale"] = float(np.float32(c["D"] ** -0.5 if rng.random() < 0.6 else rng.uniform(0.05, 0.3)))
+    c["plain"] = c["H"] == c["Hkv"] and c["window"] == 0 and c["density"] is None and rng.random() < 0.5
+    return c
+
+
+@pytest.mark.parametrize("i", range(60))
+def test_random_prefill_configuration(ta, dev, i, monkeypatch):
+    c = _prefill_case(i)
+    if c["waves"] == "auto":
+        monkeypatch.delenv("TATTN_MHA_WAVES", raising=False)
+    else:
+        monkeypatch.setenv("TATTN_MHA_WAVES", c["waves"])
+    B, H, Sq, Skv, D = c["B"], c["H"], c["Sq"], c["Skv"], c["D"]
+    x = inputs.mha_inputs(B, H, Sq, Skv, D, seed=6000 + i, sigma=c["sigma"], Hkv=c["Hkv"])
+    mask = None if c["density"] is None else inputs.block_mask(B, H, Sq, Skv, c["density"], seed=7000 + i)
+    q, k, v = (to_dev(x[n], dev) for n in "qkv")
+    o = torch.full((B, H, Sq, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device=dev)
+    if c["plain"]:
+        ta.attn_fwd(q, k, v, causal=c["causal"], scale=c["scale"], out=o, lse=lse)
+    else:
+        m = None if mask is None else torch.from_numpy(mask).to(dev)
+        ta.attn_fwd_ex(q, k, v, causal=c["causal"], scale=c["scale"], window=c["window"], block_mask=m,
+                       out=o, lse=lse)
+    torch.cuda.synchronize()
+    vals = [inputs.stored_values(x[n]) for n in "qkv"]
+    ro, rl = oracle.attention_masked(*vals, c["scale"], causal=c["causal"], window=c["window"], block_mask=mask)
+    sg = c["sigma"]
+    got, ref = to_np(o) / sg, ro / sg
+    st = parity_stats(got, to_np(lse), ref, rl)
+    msg = f"random prefill case {i} {c}: {st}"
+    # per (batch, query head): 2^-8 max|v| of its KV head, plus O's half-ulp
+    vmax = np.abs(vals[2]).max(axis=(2, 3)) / sg  # [B, Hkv]
+    vmax = np.repeat(vmax, H // c["Hkv"], axis=1)[:, :, None, None]
+    # (+ the fp32 accumulation of sum_j p_j v_j over Skv terms, <= Skv 2^-24 max|v| after the 1/l, doubled)
+    bound = 2.0 ** -8 * vmax + bf16_half_ulp(ref) + Skv * 2.0 ** -23 * vmax + 1e-5
+    assert np.all(np.abs(got - ref) <= bound), msg + f" (worst excess {(np.abs(got - ref) - bound).max():.3g})"
+    assert st["mean_o"] <= bf16_mean_o_bound(ref), msg
+    assert st["max_lse"] <= BF16_MAX_ABS_LSE, msg
+    assert st["rel_l2"] <= BF16_REL_L2_O, msg
+
+
+def _decode_case(i):
+    rng = np.random.default_rng(8000 + i)
+    B = int(rng.integers(1, 41))
+    H = int(rng.integers(1, 129))
+    lens = rng.integers(0, 3000, size=B)
+    lens[rng.random(B) < 0.15] = 0
+    return B, H, lens.astype(np.int64)
+
+
+@pytest.mark.parametrize("i", range(20))
+def test_random_decode_configuration(ta, dev, i):
+    B, H, lens = _decode_case(i)
+    rng = np.random.default_rng(9000 + i)
+    sig = np.float32(0.3)
+    n = int(lens.sum())
+    m = {"q": inputs.f32_to_bf16_bits(rng.standard_normal((B, H, 512), dtype=np.float32) * sig),
+         "q_pe": inputs.f32_to_bf16_bits(rng.standard_normal((B, H, 64), dtype=np.float32) * sig),
+         "kv": inputs.f32_to_bf16_bits(rng.standard_normal((n, 512), dtype=np.float32) * sig),
+         "k_pe": inputs.f32_to_bf16_bits(rng.standard_normal((n, 64), dtype=np.float32) * sig),
+         "indptr": np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)}
+    scale = float(np.float32(576 ** -0.5))
+    args = [to_dev(m[k], dev) for k in ("q", "q_pe", "kv", "k_pe")]
+    o = torch.full((B, H, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device=dev)
+    ta.mla_decode(*args, to_dev(m["indptr"], dev), scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    vals = [inputs.stored_values(m[k]) for k in ("q", "q_pe", "kv", "k_pe")]
+    ro, rl = oracle.mla_decode(*vals, m["indptr"], scale)
+    assert_bf16_parity(to_np(o), to_np(lse), ro, rl, f"random decode case {i} B={B} H={H} keys={n}")
+    empty = lens == 0
+    assert np.all(to_np(o)[empty] == 0) and np.all(np.isneginf(to_np(lse)[empty]))
