@@ -11,9 +11,10 @@ benchmark workload.
 Tolerance. The kernel rounds to bf16 at four points, as the reference
 Mamba-2 kernels do: the decay-weighted scores G inside a chunk, the
 decay-weighted B of the state update, the state where it meets C, and y
-itself. Each rounding is a relative error of at most 2^-9 on one term of a
-sum of up to 64 + 128 terms, so the error of y is a small multiple of 2^-9
-times the size of those terms, which is the size of y itself. The bound is
+itself. Each rounding is a relative error of at most 2^-8 (about 2^-9 on
+average) on one term of a sum of up to 64 + 128 terms, so the error of y is
+a small multiple of 2^-9 times the size of those terms, which is the size
+of y itself. The bound is
 |dy| <= 2^-8 |y| + 2^-5 rms(y) per element (rms over the head's outputs)
 and mean |dy| <= 2^-8 rms(y); for the fp32 final state, which only sees the
 rounding of B, the same form with the state's rms.
@@ -103,7 +104,14 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("Bt,L,H,G,init,final", CASES)
+def _random_case(i):
+    rng = np.random.default_rng(11000 + i)
+    G = int(rng.choice([1, 2, 4]))
+    return (int(rng.integers(1, 5)), int(rng.integers(1, 601)), G * int(rng.integers(1, 5)), G,
+            bool(rng.integers(0, 2)), bool(rng.integers(0, 2)))
+
+
+@pytest.mark.parametrize("Bt,L,H,G,init,final", CASES + [_random_case(i) for i in range(16)])
 def test_ssd_against_oracle(ta, dev, Bt, L, H, G, init, final):
     d = inputs.ssd_inputs(Bt, L, H, G, 64, 128, seed=7000 + L + H, init_state=init)
     print(f"ssd Bt={Bt} L={L} H={H} G={G} init={init} final={final}", flush=True)
