@@ -1,5 +1,5 @@
-"""Seeded random configurations of the prefill and decode entry points,
-every element compared with the float64 oracle (needs gfx950).
+"""Seeded random configurations of the prefill (bf16 and fp32) and decode
+entry points, every element compared with the float64 oracle (needs gfx950).
 
 Each case draws its own shape and options from a fixed seed: batch, query and
 KV head counts (grouped or not), ragged query and key lengths, head width,
@@ -29,8 +29,8 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.helpers import (BF16_MAX_ABS_LSE, BF16_REL_L2_O, assert_bf16_parity, bf16_half_ulp,
-                           bf16_mean_o_bound, parity_stats, to_dev, to_np)
+from tests.helpers import (BF16_MAX_ABS_LSE, BF16_REL_L2_O, assert_bf16_parity, assert_f32_parity,
+                           bf16_half_ulp, bf16_mean_o_bound, parity_stats, to_dev, to_np)
 from tiled_attention_12_amd import inputs
 
 torch = pytest.importorskip("torch")
@@ -100,6 +100,25 @@ def test_random_prefill_configuration(ta, dev, i, monkeypatch):
     assert st["mean_o"] <= bf16_mean_o_bound(ref), msg
     assert st["max_lse"] <= BF16_MAX_ABS_LSE, msg
     assert st["rel_l2"] <= BF16_REL_L2_O, msg
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_fp32_prefill_configuration(ta, dev, i):
+    # the fp32 path (no rounding of P or O): the plain fp32 gates
+    rng = np.random.default_rng(10000 + i)
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 5))
+    Sq, Skv, D = int(rng.integers(1, 400)), int(rng.integers(1, 400)), int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 2))
+    scale = float(np.float32(D ** -0.5 if rng.random() < 0.6 else rng.uniform(0.05, 0.3)))
+    x = inputs.mha_inputs(B, H, Sq, Skv, D, seed=10500 + i, dtype="f32")
+    q, k, v = (to_dev(x[n], dev) for n in "qkv")
+    o = torch.full((B, H, Sq, D), float("nan"), dtype=torch.float32, device=dev)
+    lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device=dev)
+    ta.attn_fwd_f32(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle.attention(x["q"], x["k"], x["v"], scale, causal=causal)
+    assert_f32_parity(to_np(o), to_np(lse), ro, rl, f"random fp32 case {i} B={B} H={H} {Sq}x{Skv} D={D} "
+                                                    f"causal={causal} scale={scale}")
 
 
 def _decode_case(i):
