@@ -404,6 +404,57 @@ def test_mla_streams_beyond_the_workspace_slots(ta, dev):
     assert_bf16_parity(to_np(ref[3][0]), to_np(ref[3][1]), ro, rl, "mla stream case 3")
 
 
+_TAKEOVER_SCRIPT = r"""
+import numpy as np, torch
+import tiled_attention_12_amd as ta
+from tiled_attention_12_amd import inputs
+dev = torch.device("cuda:0")
+scale = float(np.float32(576 ** -0.5))
+cases = []
+for i in range(9):
+    m = inputs.mla_inputs(2 + 3 * i, 64, seed=300 + i, kv_len_range=(1, 400 + 150 * i))
+    args = [torch.from_numpy(np.ascontiguousarray(m[k]).view(np.int16)).view(torch.bfloat16).to(dev)
+            for k in ("q", "q_pe", "kv", "k_pe")] + [torch.from_numpy(m["indptr"]).to(dev)]
+    cases.append(args)
+streams = [torch.cuda.Stream(dev) for _ in range(9)]
+# stream 0 is the only stream with a workspace at its call: no event is kept
+with torch.cuda.stream(streams[0]):
+    first = ta.mla_decode(*cases[0], scale)
+torch.cuda.synchronize()
+ref = [ta.mla_decode(*c, scale) for c in cases]  # lone calls (default stream: a second workspace)
+torch.cuda.synchronize()
+got = []
+for i in range(1, 9):  # streams 1..7 take the six free workspaces and then the least recently used
+    with torch.cuda.stream(streams[i]):
+        got.append((i, ta.mla_decode(*cases[i], scale)))
+with torch.cuda.stream(streams[0]):
+    got.append((0, ta.mla_decode(*cases[0], scale)))
+torch.cuda.synchronize()
+assert torch.equal(first[0], ref[0][0]) and torch.equal(first[1], ref[0][1])
+for i, (o, l) in got:
+    assert torch.equal(o, ref[i][0]) and torch.equal(l, ref[i][1]), i
+print("takeover ok", flush=True)
+"""
+
+
+def test_mla_workspace_takeover_after_single_stream_use(lib_path):
+    # In a fresh process: a stream's workspace whose last call came while it
+    # was the only stream with one (no completion event kept) is taken over
+    # by another stream once every workspace is in use; the takeover waits
+    # for the device on the host, and every call still gets a lone call's
+    # results. (8 workspaces per device: stream 0, the default stream and
+    # streams 1..6 fill them, stream 7 takes over stream 0's, stream 8 the
+    # next least recently used, then stream 0 takes one back.)
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=root + os.pathsep + os.environ.get("PYTHONPATH", ""))
+    r = subprocess.run([sys.executable, "-c", _TAKEOVER_SCRIPT], capture_output=True, text=True, timeout=300,
+                       cwd=root, env=env)
+    assert r.returncode == 0 and "takeover ok" in r.stdout, r.stdout[-2000:] + r.stderr[-4000:]
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_more_items_than_compute_units_without_xcd_order(ta, dev, causal):
     # B*H = 5 is not a multiple of 8, so items are taken in plain order; 5 heads

@@ -54,18 +54,24 @@ int have_device() {
 
 // Decode workspaces: one per (device, stream), up to kWsSlots streams per
 // device, each grown (never shrunk) to the largest size a call on that
-// stream has needed and kept until the process ends. `done` is recorded
-// after each call's kernels; a call first makes its stream wait for the
-// slot's last `done` (free on the same stream; it orders a slot that passes
-// to another stream when every slot is taken). A buffer that has to grow is
-// not freed at once: it is retired with its `done` event and freed by a
-// later call once that event has completed, so no call blocks the host.
+// stream has needed and kept until the process ends. A call on the slot's
+// own stream needs no ordering against the slot's earlier calls (stream
+// order gives it). Only a slot that passes to another stream (every slot
+// taken) needs its last call's completion: `done` is recorded after a call
+// whenever more than one slot is in use, and the new stream waits for it;
+// a slot whose last call came while it was the only slot in use has no
+// such event, and its takeover waits on the host for the device to finish
+// (the one case where a call blocks the host). With a single stream no
+// event is recorded or waited for. A buffer that has to grow is not freed at
+// once: it is retired with an event recorded on the calling stream, after
+// its last use, and freed by a later call once that event has completed.
 struct Workspace {
   hipStream_t stream = nullptr;
   bool used = false;
   void* ptr = nullptr;
   size_t bytes = 0;
   hipEvent_t done = nullptr;
+  bool recorded = false;  // `done` marks the slot's last call
   unsigned long long last_use = 0;
 };
 struct Retired {
@@ -238,14 +244,29 @@ TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const 
   std::lock_guard<std::mutex> lock(g_ws_mu);
   DeviceWorkspaces& d = g_ws[dev];
   free_retired(d);
+  int in_use = 0;
+  bool own = false, any_free = false;
+  for (const Workspace& x : d.slot) {
+    in_use += x.used;
+    own |= x.used && x.stream == s;
+    any_free |= !x.used;
+  }
+  const bool takeover = !own && !any_free;  // the slot passes from another stream
+  if (!own) ++in_use;
   Workspace& w = slot_for(d, s);
   w.last_use = ++d.clock;
   if (!w.done && hipEventCreateWithFlags(&w.done, hipEventDisableTiming) != hipSuccess) {
     w.done = nullptr;
     return TATTN_ERR_HIP;
   }
-  // after the slot's last call (a no-op dependency on the same stream)
-  if (hipStreamWaitEvent(s, w.done, 0) != hipSuccess) return TATTN_ERR_HIP;
+  if (takeover) {
+    // after the slot's last call on its previous stream
+    if (w.recorded) {
+      if (hipStreamWaitEvent(s, w.done, 0) != hipSuccess) return TATTN_ERR_HIP;
+    } else if (hipDeviceSynchronize() != hipSuccess) {
+      return TATTN_ERR_HIP;
+    }
+  }
   if (w.bytes < bytes) {
     void* p = nullptr;
     if (hipMalloc(&p, bytes) != hipSuccess || !p) {
@@ -253,22 +274,33 @@ TATTN_API int mla_decode(const void* q, const void* q_pe, const void* kv, const 
       return TATTN_ERR_OOM;
     }
     if (w.ptr) {
-      // the old buffer may still be in use by the slot's last call: retire it
-      // with that call's event, which takes a fresh event for the slot
-      hipEvent_t fresh = nullptr;
-      if (hipEventCreateWithFlags(&fresh, hipEventDisableTiming) != hipSuccess) {
+      // the old buffer's last use is ordered before this point of stream s
+      // (same stream, or the takeover's wait above): an event recorded here
+      // completes after it
+      hipEvent_t ret = nullptr;
+      if (hipEventCreateWithFlags(&ret, hipEventDisableTiming) != hipSuccess) {
         (void)hipFree(p);
         return TATTN_ERR_HIP;
       }
-      d.retired.push_back({w.ptr, w.done});
-      w.done = fresh;
+      if (hipEventRecord(ret, s) != hipSuccess) {
+        (void)hipEventDestroy(ret);
+        (void)hipFree(p);
+        return TATTN_ERR_HIP;
+      }
+      d.retired.push_back({w.ptr, ret});
     }
     w.ptr = p;
     w.bytes = bytes;
   }
   const hipError_t e =
       tattn::launch_mla_decode(q, q_pe, kv, k_pe, o, lse, B, H, kv_indptr, scale, n_split, w.ptr, s);
-  const hipError_t er = hipEventRecord(w.done, s);
+  // another stream may take this slot over only when several are in use
+  hipError_t er = hipSuccess;
+  w.recorded = false;
+  if (in_use > 1) {
+    er = hipEventRecord(w.done, s);
+    w.recorded = er == hipSuccess;
+  }
   if (e != hipSuccess) return status_of(e);
   return status_of(er);
 }
