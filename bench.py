@@ -38,17 +38,17 @@ MLA_SOURCES = ("tiled_attention_12_amd/csrc/mla_decode.hip", "tiled_attention_12
 TRAFFIC = {
     "mha_prefill_bf16": {"sources": MHA_SOURCES,
                          "sources_sha256": "e1d3f3c5411994f0a77b97d0e538655cdccb07c1071fdbaf9a4cfa4dab574078",
-                         "fetch_kib": 82118.8, "write_kib": 33355.8},
+                         "fetch_kib": 82119.4, "write_kib": 33305.4},
     "mha_long_causal_bf16": {"sources": MHA_SOURCES,
                              "sources_sha256": "e1d3f3c5411994f0a77b97d0e538655cdccb07c1071fdbaf9a4cfa4dab574078",
-                             "fetch_kib": 815287.1, "write_kib": 133120.8},
+                             "fetch_kib": 800855.8, "write_kib": 133120.5},
     # split + merge kernel of one call
     "mla_decode_bf16": {"sources": MLA_SOURCES,
                         "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
-                        "fetch_kib": 152247.1 + 16498.2, "write_kib": 32896.3 + 8225.8},
+                        "fetch_kib": 152247.2 + 16498.2, "write_kib": 32896.3 + 8225.8},
     "mla_decode_ragged_bf16": {"sources": MLA_SOURCES,
                                "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
-                               "fetch_kib": 667567.9 + 24533.1, "write_kib": 48959.0 + 16449.4},
+                               "fetch_kib": 667559.6 + 24533.3, "write_kib": 48959.0 + 16449.3},
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0
 
