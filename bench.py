@@ -37,10 +37,10 @@ MHA_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip", "tiled_attention_
 MLA_SOURCES = ("tiled_attention_12_amd/csrc/mla_decode.hip", "tiled_attention_12_amd/csrc/device_common.h")
 TRAFFIC = {
     "mha_prefill_bf16": {"sources": MHA_SOURCES,
-                         "sources_sha256": "e1d3f3c5411994f0a77b97d0e538655cdccb07c1071fdbaf9a4cfa4dab574078",
+                         "sources_sha256": "5d7164d7bd6de3d1dd6d8ed88fe8197285f545a495475e476762eda52620070a",
                          "fetch_kib": 82119.4, "write_kib": 33305.4},
     "mha_long_causal_bf16": {"sources": MHA_SOURCES,
-                             "sources_sha256": "e1d3f3c5411994f0a77b97d0e538655cdccb07c1071fdbaf9a4cfa4dab574078",
+                             "sources_sha256": "5d7164d7bd6de3d1dd6d8ed88fe8197285f545a495475e476762eda52620070a",
                              "fetch_kib": 800855.8, "write_kib": 133120.5},
     # split + merge kernel of one call
     "mla_decode_bf16": {"sources": MLA_SOURCES,

@@ -9,7 +9,7 @@
 // LDS stages (section 2.2 there).
 //
 // gfx950 mapping (one workgroup = NW waves = NW*32 query rows; the dense
-// launch has 8 waves, two per SIMD):
+// launch has 8 waves, two per SIMD, except on small launches, below):
 //  * S^T = K * Q^T on v_mfma_f32_32x32x16_bf16. Q^T is the B operand and is
 //    loaded once into registers; K comes from LDS as the A operand. With S
 //    transposed, lane l owns query column l%32 and 16 of the 32 keys of each
@@ -58,7 +58,9 @@
 #include "device_common.h"
 #include "launch.h"
 
-// K/V ring depth: 3 (prefetch one tile ahead) or 4 (two tiles ahead)
+// K/V ring depth of the 8-wave dense kernel and the window/mask walk: 3
+// (prefetch one tile ahead) or 4 (two tiles ahead); the 4-wave dense kernel
+// keeps two K and two V stages
 #ifndef TATTN_MHA_STAGES
 #define TATTN_MHA_STAGES 3
 #endif
