@@ -163,7 +163,8 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
  * stream's workspace and first waits for that stream's last call: on the
  * device, or, if that call came while its stream was the only one with a
  * workspace on the device, on the host until the device has finished its
- * work (the one case in which this call blocks the host).
+ * work: the one case in which this call blocks the host, and at most once
+ * per device (only a device's first workspace can be left in that state).
  */
 int mla_decode(const void* q, const void* q_pe, const void* kv, const void* k_pe,
                void* o, float* lse, int B, int H, const int32_t* kv_indptr,

@@ -61,7 +61,8 @@ int have_device() {
 // whenever more than one slot is in use, and the new stream waits for it;
 // a slot whose last call came while it was the only slot in use has no
 // such event, and its takeover waits on the host for the device to finish
-// (the one case where a call blocks the host). With a single stream no
+// (the one case where a call blocks the host; slots are never released, so
+// only a device's first slot can be in that state, and only once). With a single stream no
 // event is recorded or waited for. A buffer that has to grow is not freed at
 // once: it is retired with an event recorded on the calling stream, after
 // its last use, and freed by a later call once that event has completed.
