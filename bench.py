@@ -37,17 +37,17 @@ MHA_SOURCES = ("tiled_attention_12_amd/csrc/mha_fwd_bf16.hip", "tiled_attention_
 MLA_SOURCES = ("tiled_attention_12_amd/csrc/mla_decode.hip", "tiled_attention_12_amd/csrc/device_common.h")
 TRAFFIC = {
     "mha_prefill_bf16": {"sources": MHA_SOURCES,
-                         "sources_sha256": "5d7164d7bd6de3d1dd6d8ed88fe8197285f545a495475e476762eda52620070a",
+                         "sources_sha256": "80875f2bffcd98ae7166e70421481120b5f3a9fcec4bd8dcfc130a49c3611d4f",
                          "fetch_kib": 82119.4, "write_kib": 33305.4},
     "mha_long_causal_bf16": {"sources": MHA_SOURCES,
-                             "sources_sha256": "5d7164d7bd6de3d1dd6d8ed88fe8197285f545a495475e476762eda52620070a",
+                             "sources_sha256": "80875f2bffcd98ae7166e70421481120b5f3a9fcec4bd8dcfc130a49c3611d4f",
                              "fetch_kib": 800855.8, "write_kib": 133120.5},
     # split + merge kernel of one call
     "mla_decode_bf16": {"sources": MLA_SOURCES,
-                        "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
+                        "sources_sha256": "64b9c04fa14d7bbd561da89076c051997d1d01cf7e77e51fc1e9b87a74fc2d8a",
                         "fetch_kib": 152247.2 + 16498.2, "write_kib": 32896.3 + 8225.8},
     "mla_decode_ragged_bf16": {"sources": MLA_SOURCES,
-                               "sources_sha256": "33bb863c1b4467050d74469b7be82b1b095f0e05f44d072e77e629d58cdeff67",
+                               "sources_sha256": "64b9c04fa14d7bbd561da89076c051997d1d01cf7e77e51fc1e9b87a74fc2d8a",
                                "fetch_kib": 667559.6 + 24533.3, "write_kib": 48959.0 + 16449.3},
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0

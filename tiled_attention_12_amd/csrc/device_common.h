@@ -26,9 +26,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
-
 // Compile-time loop: f(std::integral_constant<int, i>{}) for i = 0..N-1, so
 // the body can use i as a constant expression (template arguments, asm
 // immediates).
@@ -63,13 +60,8 @@ __device__ __forceinline__ int swz(int r, int c) {
   }
 }
 
-// 16-byte direct global -> LDS load. `lds_base` must be wave-uniform; lane l
-// writes lds_base + 16*l.
-__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)gptr, (lds_void_t*)lds_base, 16, 0, 0);
-}
-
-// The same load issued through inline asm (M0 <- LDS base, then the load).
+// 16-byte direct global -> LDS load through inline asm (M0 <- LDS base, then
+// the load); lane l writes LDS base + 16*l.
 // The compiler does not see this write to LDS, so its LDS reads (including
 // the transposing-read builtin) are not made to wait for it; callers order
 // LDS reuse with wait_vmcnt() and barrier(). M0 is written here and by no
@@ -105,7 +97,7 @@ __device__ __forceinline__ u32x4 lds_read128(const void* p) {
 // ds_read_b64_tr_b16 issued through inline asm. The compiler does not see it
 // as an LDS access, so it neither counts it for lgkmcnt nor makes it wait for
 // in-flight global->LDS loads into other buffers; the caller waits with
-// wait_lds_tied() before using the result. `byte_off` is the instruction's
+// wait_lds_tied_n() before using the result. `byte_off` is the instruction's
 // immediate offset.
 template <int OFF>
 __device__ __forceinline__ u32x2 lds_read_tr16_async(uint32_t lds_addr) {
@@ -114,11 +106,6 @@ __device__ __forceinline__ u32x2 lds_read_tr16_async(uint32_t lds_addr) {
   return r;
 }
 
-// s_waitcnt lgkmcnt(0) that the listed values depend on, so no use of them
-// can be scheduled above the wait.
-__device__ __forceinline__ void wait_lds_tied(u32x2& a, u32x2& b) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
-}
 // s_waitcnt lgkmcnt(N) tied to two values: they are complete once at most N
 // later LDS operations are still outstanding (LDS operations complete in
 // order; the caller must have no scalar-memory loads in flight).
@@ -126,24 +113,6 @@ template <int N>
 __device__ __forceinline__ void wait_lds_tied_n(u32x2& a, u32x2& b) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
   asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "i"(N));
-}
-__device__ __forceinline__ void wait_lds_tied(u32x2& a, u32x2& b, u32x2& c, u32x2& d) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-}
-template <int N>
-__device__ __forceinline__ void wait_lds_tied(u32x2 (&r)[N]) {
-  static_assert(N % 4 == 0, "groups of 4");
-  if constexpr (N == 4) {
-    wait_lds_tied(r[0], r[1], r[2], r[3]);
-  } else {
-    asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(r[0]), "+v"(r[1]), "+v"(r[2]), "+v"(r[3]),
-                 "+v"(r[4]), "+v"(r[5]), "+v"(r[6]), "+v"(r[7]));
-    if constexpr (N > 8) {
-      static_assert(N == 16, "up to 16 values");
-      asm volatile("" : "+v"(r[8]), "+v"(r[9]), "+v"(r[10]), "+v"(r[11]), "+v"(r[12]),
-                   "+v"(r[13]), "+v"(r[14]), "+v"(r[15]));
-    }
-  }
 }
 
 // ds_read_b128 through inline asm (not counted by the compiler; wait with
