@@ -44,10 +44,10 @@ TRAFFIC = {
                              "fetch_kib": 800855.8, "write_kib": 133120.5},
     # split + merge kernel of one call
     "mla_decode_bf16": {"sources": MLA_SOURCES,
-                        "sources_sha256": "64b9c04fa14d7bbd561da89076c051997d1d01cf7e77e51fc1e9b87a74fc2d8a",
+                        "sources_sha256": "2bf1c3ec81376fd2f5e31e3a97d0034be7db53fc28339c22194c5cef33aca193",
                         "fetch_kib": 152247.2 + 16498.2, "write_kib": 32896.3 + 8225.8},
     "mla_decode_ragged_bf16": {"sources": MLA_SOURCES,
-                               "sources_sha256": "64b9c04fa14d7bbd561da89076c051997d1d01cf7e77e51fc1e9b87a74fc2d8a",
+                               "sources_sha256": "2bf1c3ec81376fd2f5e31e3a97d0034be7db53fc28339c22194c5cef33aca193",
                                "fetch_kib": 667559.6 + 24533.3, "write_kib": 48959.0 + 16449.3},
 }
 FETCH_FACTOR, WRITE_FACTOR = 2.0, 1.0

@@ -214,7 +214,12 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(MlaArgs a, int P) {
 // accumulation registers, which O fills, and no accumulator is moved
 // between the two register files inside the tile loop. LAST appends the
 // wait states a VALU access to the result needs after the final MFMA of a
-// chain (the compiler does not see this MFMA).
+// chain (the compiler does not see this MFMA). For the same reason no wait
+// states protect the A and B operands: an MFMA of the chain may read them
+// some clocks after it issues, so no VALU instruction may run between these
+// MFMAs (the compiler could give its result a register an MFMA has yet to
+// read); the only writes there are the next K fragments' LDS reads, whose
+// data lands long after.
 template <bool FIRST, bool LAST>
 __device__ __forceinline__ void mfma32_v(f32x16& s, bf16x8 a, bf16x8 b) {
   if constexpr (FIRST && LAST)
