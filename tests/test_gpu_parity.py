@@ -615,3 +615,17 @@ def test_mla_workspace_cap_reports_oom_and_writes_nothing(ta, dev, monkeypatch):
     torch.cuda.synchronize()
     ro, rl = oracle.mla_decode(*_mla_vals(m), m["indptr"], 0.05)
     assert_bf16_parity(to_np(o), to_np(l2), ro, rl, "mla after the capped call")
+
+
+def test_explicit_stream_gives_the_default_stream_result(ta, dev):
+    # a caller's own stream (same device) is used for the launch; the result
+    # is bit-identical to the call on the current stream
+    x = inputs.mha_inputs(1, 4, 300, 300, 128, seed=8800)
+    q, k, v = (to_dev(x[n], dev) for n in "qkv")
+    o0, l0 = ta.attn_fwd(q, k, v, causal=True)
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    o1, l1 = ta.attn_fwd(q, k, v, causal=True, stream=s)
+    s.synchronize()
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)

@@ -2,7 +2,8 @@
 
 Every function here checks dtypes, devices, shapes and contiguity of torch
 tensors, allocates outputs with torch, and passes raw device pointers plus
-the current HIP stream to the C ABI. All arithmetic runs in the library's
+the HIP stream (the caller's, else the device's current one) to the C ABI,
+with the tensors' device made current for the call. All arithmetic runs in the library's
 gfx950 kernels; if the library is missing, loading this module fails.
 """
 
@@ -72,10 +73,16 @@ def _torch():
     return torch
 
 
-def _stream_ptr(device, stream):
+def _launch(fn, device, stream, *args):
+    """Calls fn(*args, stream handle) with the tensors' device current: the
+    library launches on the current device, so tensors on another device
+    than the current one are handled by switching to theirs for the call."""
     torch = _torch()
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None and stream.device != device:
+        raise ValueError(f"stream is on {stream.device}, the tensors on {device}")
+    with torch.cuda.device(device):
+        s = torch.cuda.current_stream(device) if stream is None else stream
+        return fn(*args, ctypes.c_void_p(s.cuda_stream))
 
 
 def _ptr(t):
@@ -113,8 +120,8 @@ def _mha(fn_name, q, k, v, causal, scale, out, lse, stream, dtype):
     if tuple(out.shape) != (B, H, Sq, D) or tuple(lse.shape) != (B, H, Sq):
         raise ValueError("out/lse have the wrong shape")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    rc = getattr(_LIB, fn_name)(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq, Skv, D,
-                                int(bool(causal)), ctypes.c_float(scale), _stream_ptr(dev, stream))
+    rc = _launch(getattr(_LIB, fn_name), dev, stream, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Sq,
+                 Skv, D, int(bool(causal)), ctypes.c_float(scale))
     if rc != TATTN_OK:
         raise TattnError(rc, fn_name)
     return out, lse
@@ -153,9 +160,8 @@ def attn_fwd_ex(q, k, v, causal=False, scale=None, window=0, block_mask=None, ou
     if tuple(out.shape) != (B, H, Sq, D) or tuple(lse.shape) != (B, H, Sq):
         raise ValueError("out/lse have the wrong shape")
     scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
-    rc = _LIB.attn_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Sq, Skv, D,
-                          int(bool(causal)), int(window), _ptr(block_mask), ctypes.c_float(scale),
-                          _stream_ptr(dev, stream))
+    rc = _launch(_LIB.attn_fwd_ex, dev, stream, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Sq,
+                 Skv, D, int(bool(causal)), int(window), _ptr(block_mask), ctypes.c_float(scale))
     if rc != TATTN_OK:
         raise TattnError(rc, "attn_fwd_ex")
     return out, lse
@@ -190,8 +196,8 @@ def _mla(fn_name, q, q_pe, kv, k_pe, kv_indptr, scale, out, lse, stream):
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     _check_dev("out", out, torch.bfloat16, dev)
     _check_dev("lse", lse, torch.float32, dev)
-    rc = getattr(_LIB, fn_name)(_ptr(q), _ptr(q_pe), _ptr(kv), _ptr(k_pe), _ptr(out), _ptr(lse), B, H,
-                                _ptr(kv_indptr), ctypes.c_float(float(scale)), _stream_ptr(dev, stream))
+    rc = _launch(getattr(_LIB, fn_name), dev, stream, _ptr(q), _ptr(q_pe), _ptr(kv), _ptr(k_pe), _ptr(out),
+                 _ptr(lse), B, H, _ptr(kv_indptr), ctypes.c_float(float(scale)))
     if rc != TATTN_OK:
         raise TattnError(rc, fn_name)
     return out, lse
@@ -243,8 +249,8 @@ def ssd_scan(x, dt, A, B, C, init_state=None, final_state=False, out=None, strea
     _check_dev("out", out, torch.bfloat16, dev)
     if tuple(out.shape) != (Bt, L, H, P):
         raise ValueError("out has the wrong shape")
-    rc = _LIB.ssd_scan(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(out), _ptr(init_state), _ptr(fs),
-                       Bt, L, H, G, P, N, _stream_ptr(dev, stream))
+    rc = _launch(_LIB.ssd_scan, dev, stream, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(out),
+                 _ptr(init_state), _ptr(fs), Bt, L, H, G, P, N)
     if rc != TATTN_OK:
         raise TattnError(rc, "ssd_scan")
     return (out, fs) if fs is not None else out
