@@ -9,7 +9,9 @@
  *
  * Pointers named as device pointers must point to device memory (for example
  * from hipMalloc or torch on a ROCm device); `stream` is a hipStream_t passed
- * as void* (NULL selects the default stream of the current device). The
+ * as void* (NULL selects the default stream of the current device). Kernels
+ * run on the calling thread's current device: the pointers and the stream
+ * must belong to it (the library cannot check that). The
  * library never frees, retains or reallocates caller memory; outputs are
  * fully overwritten (never accumulated into). Calls are reentrant and may be
  * issued concurrently on different streams. attn_fwd, attn_fwd_ex,
