@@ -1,11 +1,11 @@
-"""Tensors past 4 GiB: the prefill's K/V, its Q/O and the scan's x/y each
-span more than 2^32 bytes, so every byte offset past 2^31 and 2^32 is
-exercised (needs gfx950 and ~20 GB of device memory).
+"""Tensors past 4 GiB: the prefill's K/V, its Q/O, the decode's latent key
+rows and the scan's x/y each span more than 2^32 bytes, so byte offsets past
+2^31 and 2^32 are exercised (needs gfx950 and ~20 GB of device memory).
 
 Only a few heads carry seeded random data (the first, a middle and the last,
 whose data sits past 4 GiB); the others are zero, which gives outputs with a
-closed form (uniform softmax: O = the mean of V, LSE = ln(keys); a zero scan
-input: y = 0). Outputs start as NaN, so an element no workgroup wrote fails.
+closed form (uniform softmax: O = the mean of V, LSE = ln(keys); zero keys
+and values: O = 0; a zero scan input: y = 0). Outputs start as NaN, so an element no workgroup wrote fails.
 The random heads are compared with the float64 oracle.
 """
 
@@ -154,4 +154,44 @@ def test_scan_inputs_and_outputs_past_4_gib(ta, dev):
     # zero inputs give zero outputs
     assert not torch.count_nonzero(y[0, :, 1:H - 1]).item()
     del x, y
+    torch.cuda.empty_cache()
+
+
+def test_mla_key_rows_past_4_gib(ta, dev):
+    # 80 batches x 65,536 keys: 5.4 GB of latent rows (the last batch's start
+    # 5.0 GiB in) and 0.7 GB of rotary rows; batches 0, 41 and 79 random, the
+    # rest zero (O = 0, LSE = ln(keys))
+    B, H, n = 80, 128, 1 << 16
+    print(f"large MLA: B={B} H={H} keys per batch={n}", flush=True)
+    rng = np.random.default_rng(9400)
+    sig = np.float32(0.3)
+    qb = inputs.f32_to_bf16_bits(rng.standard_normal((B, H, 512), dtype=np.float32) * sig)
+    qpb = inputs.f32_to_bf16_bits(rng.standard_normal((B, H, 64), dtype=np.float32) * sig)
+    kv = torch.zeros((B * n, 512), dtype=torch.bfloat16, device=dev)
+    kpe = torch.zeros((B * n, 64), dtype=torch.bfloat16, device=dev)
+    rows = {}
+    for b in (0, 41, B - 1):
+        kvb = inputs.f32_to_bf16_bits(rng.standard_normal((n, 512), dtype=np.float32) * sig)
+        kpb = inputs.f32_to_bf16_bits(rng.standard_normal((n, 64), dtype=np.float32) * sig)
+        _put(kv, slice(b * n, (b + 1) * n), kvb)
+        _put(kpe, slice(b * n, (b + 1) * n), kpb)
+        rows[b] = (inputs.stored_values(kvb), inputs.stored_values(kpb))
+    indptr = torch.arange(0, (B + 1) * n, n, dtype=torch.int32, device=dev)
+    q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).to(dev)
+    qpe = torch.from_numpy(qpb.view(np.int16)).view(torch.bfloat16).to(dev)
+    o = torch.full((B, H, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device=dev)
+    scale = float(np.float32(576 ** -0.5))
+    ta.mla_decode(q, qpe, kv, kpe, indptr, scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    on, ln = to_np(o), to_np(lse)
+    assert not np.isnan(on).any() and not np.isnan(ln).any()
+    qv, qpv = inputs.stored_values(qb), inputs.stored_values(qpb)
+    for b, (kvv, kpv) in rows.items():
+        ro, rl = oracle.mla_decode(qv[b:b + 1], qpv[b:b + 1], kvv, kpv, np.array([0, n], np.int32), scale)
+        assert_bf16_parity(on[b:b + 1], ln[b:b + 1], ro, rl, f"large MLA batch {b}")
+    zero = [b for b in range(B) if b not in rows]
+    assert np.all(on[zero] == 0.0)
+    assert np.abs(ln[zero] - math.log(n)).max() <= 1e-5
+    del kv, kpe
     torch.cuda.empty_cache()
