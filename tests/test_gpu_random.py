@@ -25,6 +25,8 @@ inputs (max|v| ~ 4.5) the bound is ~0.018 plus the half-ulp; the errors
 measured there stay under 1e-2, and the configuration tests hold them to it.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -35,6 +37,11 @@ from tiled_attention_12_amd import inputs
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
+
+# how many seeded cases of each kind run; TATTN_RANDOM_SCALE multiplies the
+# defaults for a longer sweep (the seeds of the default cases stay the same)
+_SCALE = max(1, int(os.environ.get("TATTN_RANDOM_SCALE", "1")))
+N_PREFILL, N_FP32, N_DECODE = 60 * _SCALE, 12 * _SCALE, 20 * _SCALE
 
 
 @pytest.fixture(scope="module")
@@ -65,7 +72,7 @@ def _prefill_case(i):
     return c
 
 
-@pytest.mark.parametrize("i", range(60))
+@pytest.mark.parametrize("i", range(N_PREFILL))
 def test_random_prefill_configuration(ta, dev, i, monkeypatch):
     c = _prefill_case(i)
     if c["waves"] == "auto":
@@ -102,7 +109,7 @@ def test_random_prefill_configuration(ta, dev, i, monkeypatch):
     assert st["rel_l2"] <= BF16_REL_L2_O, msg
 
 
-@pytest.mark.parametrize("i", range(12))
+@pytest.mark.parametrize("i", range(N_FP32))
 def test_random_fp32_prefill_configuration(ta, dev, i):
     # the fp32 path (no rounding of P or O): the plain fp32 gates
     rng = np.random.default_rng(10000 + i)
@@ -130,7 +137,7 @@ def _decode_case(i):
     return B, H, lens.astype(np.int64)
 
 
-@pytest.mark.parametrize("i", range(20))
+@pytest.mark.parametrize("i", range(N_DECODE))
 def test_random_decode_configuration(ta, dev, i):
     B, H, lens = _decode_case(i)
     rng = np.random.default_rng(9000 + i)

@@ -18,6 +18,8 @@ under its expected size; the fp32 final state, which sees only the rounding
 of B, is bounded the same way.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -118,7 +120,10 @@ def _random_case(i):
             bool(rng.integers(0, 2)), bool(rng.integers(0, 2)))
 
 
-@pytest.mark.parametrize("Bt,L,H,G,init,final", CASES + [_random_case(i) for i in range(16)])
+_N_RANDOM = 16 * max(1, int(os.environ.get("TATTN_RANDOM_SCALE", "1")))  # more for a longer sweep
+
+
+@pytest.mark.parametrize("Bt,L,H,G,init,final", CASES + [_random_case(i) for i in range(_N_RANDOM)])
 def test_ssd_against_oracle(ta, dev, Bt, L, H, G, init, final):
     d = inputs.ssd_inputs(Bt, L, H, G, 64, 128, seed=7000 + L + H, init_state=init)
     print(f"ssd Bt={Bt} L={L} H={H} G={G} init={init} final={final}", flush=True)
