@@ -141,6 +141,7 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
  *   q_pe      device, bf16 [B, H, 64],  16-byte aligned
  *   kv        device, bf16 [N, 512],    16-byte aligned, N = kv_indptr[B]
  *   k_pe      device, bf16 [N, 64],     16-byte aligned
+ *             (kv and k_pe may be NULL when N = 0: no batch has keys)
  *   o         device, bf16 [B, H, 512], 16-byte aligned, written
  *   lse       device, fp32 [B, H],      4-byte aligned, written
  *   B >= 0 (0: nothing to do); 1 <= H <= 128 (else TATTN_ERR_UNSUPPORTED)

@@ -82,6 +82,8 @@ int main() {
          TATTN_OK);
   expect("mla valid, no device",
          mla_decode(P(16), P(16), P(16), P(16), P(16), F(16), 2, 128, I(16), 0.05f, nullptr), TATTN_ERR_HIP);
+  expect("mla no keys (null kv, k_pe), no device",
+         mla_decode(P(16), P(16), nullptr, nullptr, P(16), F(16), 2, 128, I(16), 0.05f, nullptr), TATTN_ERR_HIP);
   expect("mla noalloc H=129", mla_decode_noalloc(P(16), P(16), P(16), P(16), P(16), F(16), 2, 129, I(16), 0.05f,
                                                  nullptr),
          TATTN_ERR_UNSUPPORTED);

@@ -105,6 +105,9 @@ def test_mla_argument_validation(L, fn):
     assert call(kv=40) == ALIGN
     assert call(ind=2) == ALIGN
     assert call(B=0, q=None) == OK
+    # no keys in any batch: kv and k_pe may be null (validation passes; on a
+    # machine without a GPU the call then reports the missing device)
+    assert call(kv=None, kpe=None) in (OK, HIP)
 
 
 def test_ssd_argument_validation(L):

@@ -629,3 +629,21 @@ def test_explicit_stream_gives_the_default_stream_result(ta, dev):
     s.synchronize()
     torch.cuda.synchronize()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
+
+
+@pytest.mark.parametrize("fn", ["mla_decode", "mla_decode_noalloc"])
+@pytest.mark.parametrize("B,H", [(1, 7), (5, 128)])
+def test_mla_no_keys_in_any_batch(ta, dev, fn, B, H):
+    # every batch empty (N = 0): kv and k_pe are empty tensors (null pointers
+    # at the C ABI); every row gets O = 0 and LSE = -inf
+    rng = np.random.default_rng(8900 + B)
+    q = to_dev(inputs.f32_to_bf16_bits(rng.standard_normal((B, H, 512), dtype=np.float32)), dev)
+    qpe = to_dev(inputs.f32_to_bf16_bits(rng.standard_normal((B, H, 64), dtype=np.float32)), dev)
+    kv = torch.empty((0, 512), dtype=torch.bfloat16, device=dev)
+    kpe = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    indptr = torch.zeros(B + 1, dtype=torch.int32, device=dev)
+    o = torch.full((B, H, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device=dev)
+    getattr(ta, fn)(q, qpe, kv, kpe, indptr, 576 ** -0.5, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0).item() and torch.all(torch.isneginf(lse)).item()

@@ -219,7 +219,9 @@ static int check_mla(const void* q, const void* q_pe, const void* kv, const void
     return TATTN_OK;
   }
   if (H < 1 || H > 128) return TATTN_ERR_UNSUPPORTED;
-  if (!q || !q_pe || !kv || !k_pe || !o || !lse || !kv_indptr) return TATTN_ERR_INVALID_ARG;
+  // kv and k_pe may be null when no batch has keys (N = 0): the kernels read
+  // key rows only inside the ranges kv_indptr gives
+  if (!q || !q_pe || !o || !lse || !kv_indptr) return TATTN_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(q_pe, 16) || !aligned(kv, 16) || !aligned(k_pe, 16) || !aligned(o, 16) ||
       !aligned(lse, 4) || !aligned(kv_indptr, 4))
     return TATTN_ERR_ALIGN;
