@@ -41,7 +41,7 @@ pytestmark = pytest.mark.gpu
 # how many seeded cases of each kind run; TATTN_RANDOM_SCALE multiplies the
 # defaults for a longer sweep (the seeds of the default cases stay the same)
 _SCALE = max(1, int(os.environ.get("TATTN_RANDOM_SCALE", "1")))
-N_PREFILL, N_FP32, N_DECODE = 60 * _SCALE, 12 * _SCALE, 20 * _SCALE
+N_PREFILL, N_FP32, N_DECODE, N_MANY = 60 * _SCALE, 12 * _SCALE, 20 * _SCALE, 8 * _SCALE
 
 
 @pytest.fixture(scope="module")
@@ -107,6 +107,62 @@ def test_random_prefill_configuration(ta, dev, i, monkeypatch):
     assert st["mean_o"] <= bf16_mean_o_bound(ref), msg
     assert st["max_lse"] <= BF16_MAX_ABS_LSE, msg
     assert st["rel_l2"] <= BF16_REL_L2_O, msg
+
+
+def _many_items_case(i):
+    rng = np.random.default_rng(12000 + i)
+    hkv = int(rng.choice([2, 4, 8, 16]))
+    c = {"B": int(rng.integers(1, 5)), "Hkv": hkv, "H": hkv * int(rng.choice([1, 2, 4, 8])),
+         "Sq": int(rng.integers(600, 3001)), "D": int(rng.choice([64, 128])), "causal": bool(rng.integers(0, 2)),
+         "window": int(rng.integers(1, 1200)) if rng.random() < 0.3 else 0,
+         "density": float(rng.uniform(0.2, 0.9)) if rng.random() < 0.25 else None,
+         "waves": str(rng.choice(["auto", "4", "8"]))}
+    c["Skv"] = c["Sq"] if rng.random() < 0.5 else int(rng.integers(600, 3001))
+    c["H"] = min(c["H"], 64)
+    return c
+
+
+@pytest.mark.parametrize("i", range(N_MANY))
+def test_random_prefill_with_many_work_items(ta, dev, i, monkeypatch):
+    # larger launches, most with more work items than compute units (the
+    # persistent workgroups loop over several items, in the XCD and causal
+    # orders):
+    # every output written (NaN-prefilled), three sampled heads against the
+    # oracle under the same bounds as the configuration tests above
+    c = _many_items_case(i)
+    if c["waves"] == "auto":
+        monkeypatch.delenv("TATTN_MHA_WAVES", raising=False)
+    else:
+        monkeypatch.setenv("TATTN_MHA_WAVES", c["waves"])
+    B, H, Hkv, Sq, Skv, D = c["B"], c["H"], c["Hkv"], c["Sq"], c["Skv"], c["D"]
+    print(f"many items case {i}: {c}", flush=True)
+    x = inputs.mha_inputs(B, H, Sq, Skv, D, seed=12500 + i, Hkv=Hkv)
+    mask = None if c["density"] is None else inputs.block_mask(B, H, Sq, Skv, c["density"], seed=13000 + i)
+    q, k, v = (to_dev(x[n], dev) for n in "qkv")
+    o = torch.full((B, H, Sq, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H, Sq), float("nan"), dtype=torch.float32, device=dev)
+    scale = float(np.float32(D ** -0.5))
+    m = None if mask is None else torch.from_numpy(mask).to(dev)
+    ta.attn_fwd_ex(q, k, v, causal=c["causal"], scale=scale, window=c["window"], block_mask=m, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item(), f"case {i}: unwritten outputs"
+    rng = np.random.default_rng(14000 + i)
+    picks = [(0, 0), (B - 1, H - 1), (int(rng.integers(B)), int(rng.integers(H)))]
+    for b, h in picks:
+        kh = h // (H // Hkv)
+        mk = None if mask is None else mask[b:b + 1, h:h + 1]
+        qh = inputs.stored_values(x["q"][b:b + 1, h:h + 1])
+        kk, vv = (inputs.stored_values(x[n][b:b + 1, kh:kh + 1]) for n in "kv")
+        ro, rl = oracle.attention_masked(qh, kk, vv, scale, causal=c["causal"], window=c["window"], block_mask=mk)
+        got, got_l = to_np(o[b:b + 1, h:h + 1]), to_np(lse[b:b + 1, h:h + 1])
+        st = parity_stats(got, got_l, ro, rl)
+        msg = f"many items case {i} {c} head ({b}, {h}): {st}"
+        vmax = np.abs(vv).max()
+        bound = 2.0 ** -8 * vmax + bf16_half_ulp(ro) + Skv * 2.0 ** -23 * vmax + 1e-5
+        assert np.all(np.abs(got - ro) <= bound), msg
+        assert st["mean_o"] <= bf16_mean_o_bound(ro), msg
+        assert st["max_lse"] <= BF16_MAX_ABS_LSE, msg
+        assert st["rel_l2"] <= BF16_REL_L2_O, msg
 
 
 @pytest.mark.parametrize("i", range(N_FP32))
