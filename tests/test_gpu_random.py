@@ -42,6 +42,7 @@ pytestmark = pytest.mark.gpu
 # defaults for a longer sweep (the seeds of the default cases stay the same)
 _SCALE = max(1, int(os.environ.get("TATTN_RANDOM_SCALE", "1")))
 N_PREFILL, N_FP32, N_DECODE, N_MANY = 60 * _SCALE, 12 * _SCALE, 20 * _SCALE, 8 * _SCALE
+N_BIG_DECODE = 4 * _SCALE
 
 
 @pytest.fixture(scope="module")
@@ -215,3 +216,40 @@ def test_random_decode_configuration(ta, dev, i):
     assert_bf16_parity(to_np(o), to_np(lse), ro, rl, f"random decode case {i} B={B} H={H} keys={n}")
     empty = lens == 0
     assert np.all(to_np(o)[empty] == 0) and np.all(np.isneginf(to_np(lse)[empty]))
+
+
+@pytest.mark.parametrize("i", range(N_BIG_DECODE))
+def test_random_decode_with_many_batches(ta, dev, i):
+    # 900-1300 batches: both sides of the batch count at which the split plan
+    # moves from the split workgroups into a kernel of its own; every output
+    # written (NaN-prefilled), empty batches exact, eight batches against the
+    # oracle one at a time
+    rng = np.random.default_rng(15000 + i)
+    B, H = int(rng.integers(900, 1301)), int(rng.integers(1, 129))
+    lens = rng.integers(0, 400, size=B)
+    lens[rng.random(B) < 0.15] = 0
+    n = int(lens.sum())
+    print(f"many-batch decode case {i}: B={B} H={H} keys={n}", flush=True)
+    sig = np.float32(0.3)
+    m = {"q": inputs.f32_to_bf16_bits(rng.standard_normal((B, H, 512), dtype=np.float32) * sig),
+         "q_pe": inputs.f32_to_bf16_bits(rng.standard_normal((B, H, 64), dtype=np.float32) * sig),
+         "kv": inputs.f32_to_bf16_bits(rng.standard_normal((n, 512), dtype=np.float32) * sig),
+         "k_pe": inputs.f32_to_bf16_bits(rng.standard_normal((n, 64), dtype=np.float32) * sig)}
+    indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    scale = float(np.float32(576 ** -0.5))
+    o = torch.full((B, H, 512), float("nan"), dtype=torch.bfloat16, device=dev)
+    lse = torch.full((B, H), float("nan"), dtype=torch.float32, device=dev)
+    ta.mla_decode(*(to_dev(m[k], dev) for k in ("q", "q_pe", "kv", "k_pe")), to_dev(indptr, dev), scale,
+                  out=o, lse=lse)
+    torch.cuda.synchronize()
+    on, ln = to_np(o), to_np(lse)
+    assert not np.isnan(on).any() and not np.isnan(ln).any(), f"case {i}: unwritten outputs"
+    empty = lens == 0
+    assert np.all(on[empty] == 0) and np.all(np.isneginf(ln[empty]))
+    picks = sorted({0, B - 1, *(int(b) for b in rng.integers(0, B, size=6))})
+    for b in picks:
+        lo, hi = indptr[b], indptr[b + 1]
+        ro, rl = oracle.mla_decode(*(inputs.stored_values(m[k][b:b + 1]) for k in ("q", "q_pe")),
+                                   *(inputs.stored_values(m[k][lo:hi]) for k in ("kv", "k_pe")),
+                                   np.array([0, hi - lo], np.int32), scale)
+        assert_bf16_parity(on[b:b + 1], ln[b:b + 1], ro, rl, f"many-batch decode case {i} batch {b} ({hi - lo} keys)")
