@@ -196,3 +196,29 @@ def test_ssd_continuation_matches_one_pass(ta, dev):
     y2, f2 = _run(ta, dev, second, final=True)
     ry2, rf2 = ossd.ssd_recurrence(*_ref_inputs(second), second["init_state"])
     _check_all(second, y2, ry2, "second half", f2, rf2)
+
+
+_N_LARGER = 4 * max(1, int(os.environ.get("TATTN_RANDOM_SCALE", "1")))
+
+
+@pytest.mark.parametrize("i", range(_N_LARGER))
+def test_ssd_random_larger_launch(ta, dev, i):
+    # larger seeded launches, often with more workgroups than compute units:
+    # every output written (NaN-prefilled), three heads against the recurrence
+    rng = np.random.default_rng(16000 + i)
+    G = int(rng.choice([1, 2, 4]))
+    Bt, L, H = int(rng.integers(1, 9)), int(rng.integers(500, 3001)), G * int(rng.integers(4, 25))
+    init, final = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    print(f"larger scan case {i}: Bt={Bt} L={L} H={H} G={G} init={init} final={final}", flush=True)
+    d = inputs.ssd_inputs(Bt, L, H, G, 64, 128, seed=16500 + i, init_state=init)
+    x, B, C = (to_dev(d[n], dev) for n in ("x", "B", "C"))
+    dt, A = to_dev(d["dt"], dev), to_dev(d["A"], dev)
+    s0 = to_dev(d["init_state"], dev) if init else None
+    y = torch.full((Bt, L, H, 64), float("nan"), dtype=torch.bfloat16, device=dev)
+    fs = torch.full((Bt, H, 64, 128), float("nan"), dtype=torch.float32, device=dev) if final else False
+    r = ta.ssd_scan(x, dt, A, B, C, init_state=s0, final_state=fs, out=y)
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any().item() and (not final or not torch.isnan(fs).any().item())
+    pairs = [(0, 0), (Bt - 1, H - 1), (int(rng.integers(Bt)), int(rng.integers(H)))]
+    ry, rf = _recurrence_heads(d, pairs)
+    _check(d, pairs, to_np(y), ry, f"larger scan case {i}", to_np(r[1]) if final else None, rf if final else None)
