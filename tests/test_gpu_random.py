@@ -253,3 +253,43 @@ def test_random_decode_with_many_batches(ta, dev, i):
                                    *(inputs.stored_values(m[k][lo:hi]) for k in ("kv", "k_pe")),
                                    np.array([0, hi - lo], np.int32), scale)
         assert_bf16_parity(on[b:b + 1], ln[b:b + 1], ro, rl, f"many-batch decode case {i} batch {b} ({hi - lo} keys)")
+
+
+N_STREAMS_CASES = 2 * _SCALE
+
+
+@pytest.mark.parametrize("i", range(N_STREAMS_CASES))
+def test_random_decode_calls_over_many_streams(ta, dev, i):
+    # 40 decode calls of random sizes spread over 10 streams (more than the
+    # library's 8 workspace slots, so slots pass between streams and grow):
+    # every result equals the same call made alone on the current stream, bit
+    # for bit (the split depends only on the device, not on the stream)
+    rng = np.random.default_rng(17000 + i)
+    sig = np.float32(0.3)
+    shapes = []
+    for _ in range(6):
+        B, H = int(rng.integers(1, 300)), int(rng.integers(1, 129))
+        lens = rng.integers(0, 800, size=B)
+        n = int(lens.sum())
+        m = {"q": rng.standard_normal((B, H, 512), dtype=np.float32) * sig,
+             "q_pe": rng.standard_normal((B, H, 64), dtype=np.float32) * sig,
+             "kv": rng.standard_normal((n, 512), dtype=np.float32) * sig,
+             "k_pe": rng.standard_normal((n, 64), dtype=np.float32) * sig}
+        args = [to_dev(inputs.f32_to_bf16_bits(m[k]), dev) for k in ("q", "q_pe", "kv", "k_pe")]
+        args.append(to_dev(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32), dev))
+        shapes.append((B, H, args))
+    scale = float(np.float32(576 ** -0.5))
+    refs = []
+    for B, H, args in shapes:
+        refs.append(ta.mla_decode(*args, scale))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in range(10)]
+    calls = [(int(rng.integers(len(shapes))), int(rng.integers(len(streams)))) for _ in range(40)]
+    outs = [(torch.empty((shapes[k][0], shapes[k][1], 512), dtype=torch.bfloat16, device=dev),
+             torch.empty((shapes[k][0], shapes[k][1]), dtype=torch.float32, device=dev)) for k, _ in calls]
+    torch.cuda.synchronize()
+    for (k, s), (o, lse) in zip(calls, outs):
+        ta.mla_decode(*shapes[k][2], scale, out=o, lse=lse, stream=streams[s])
+    torch.cuda.synchronize()
+    for j, ((k, s), (o, lse)) in enumerate(zip(calls, outs)):
+        assert torch.equal(o, refs[k][0]) and torch.equal(lse, refs[k][1]), f"case {i} call {j} (shape {k}, stream {s})"
