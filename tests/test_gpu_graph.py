@@ -6,6 +6,8 @@ between, on new inputs copied into the captured buffers, and every replay
 must equal the eager call bit for bit.
 """
 
+import os
+
 import numpy as np
 import pytest
 
@@ -114,4 +116,61 @@ def test_mla_decode_noalloc_in_a_graph(ta, dev):
             return ta.mla_decode(b["q"], b["q_pe"], b["kv"], b["k_pe"], ind, scale)
         return ta.mla_decode_noalloc(b["q"], b["q_pe"], b["kv"], b["k_pe"], ind, scale, out=o, lse=lse)
 
+    _capture_and_replay(dev, call, bufs, xs[1:] + xs[:1])
+
+
+_N_RANDOM = 6 * max(1, int(os.environ.get("TATTN_RANDOM_SCALE", "1")))
+
+
+@pytest.mark.parametrize("i", range(_N_RANDOM))
+def test_random_entry_point_in_a_graph(ta, dev, i):
+    # a seeded random entry point and shape, captured and replayed as above
+    rng = np.random.default_rng(18000 + i)
+    kind = ("attn_fwd", "attn_fwd_ex", "mla_decode_noalloc")[i % 3]
+    if kind == "mla_decode_noalloc":
+        B, H = int(rng.integers(1, 60)), int(rng.integers(1, 129))
+        lens = rng.integers(0, 1500, size=B)
+        indptr = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        n = int(indptr[-1])
+        xs = []
+        for r in range(3):
+            g = np.random.default_rng(18500 + 10 * i + r)
+            xs.append({k: to_dev(inputs.f32_to_bf16_bits(g.standard_normal(shape, dtype=np.float32) * np.float32(0.3)),
+                                 dev)
+                       for k, shape in (("q", (B, H, 512)), ("q_pe", (B, H, 64)), ("kv", (n, 512)),
+                                        ("k_pe", (n, 64)))})
+        ind = to_dev(indptr, dev)
+        o = torch.empty((B, H, 512), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+        scale = float(np.float32(576 ** -0.5))
+
+        def call(b, fresh=False):
+            if fresh:
+                return ta.mla_decode(b["q"], b["q_pe"], b["kv"], b["k_pe"], ind, scale)
+            return ta.mla_decode_noalloc(b["q"], b["q_pe"], b["kv"], b["k_pe"], ind, scale, out=o, lse=lse)
+    else:
+        hkv = int(rng.choice([1, 2, 4]))
+        B, H = int(rng.integers(1, 4)), hkv * int(rng.choice([1, 2, 4]))
+        Sq, Skv, D = int(rng.integers(1, 900)), int(rng.integers(1, 900)), int(rng.choice([64, 128]))
+        causal = bool(rng.integers(0, 2))
+        if kind == "attn_fwd":
+            hkv = H
+        window = int(rng.integers(1, 500)) if kind == "attn_fwd_ex" and rng.random() < 0.5 else 0
+        mask = (torch.from_numpy(inputs.block_mask(B, H, Sq, Skv, 0.6, seed=18600 + i)).to(dev)
+                if kind == "attn_fwd_ex" and rng.random() < 0.5 else None)
+        xs = [{n: to_dev(inputs.mha_inputs(B, H, Sq, Skv, D, seed=18700 + 10 * i + r, Hkv=hkv)[n], dev)
+               for n in "qkv"} for r in range(3)]
+        o = torch.empty_like(xs[0]["q"])
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+        kw = dict(causal=causal, scale=0.09)
+        if kind == "attn_fwd_ex":
+            kw.update(window=window, block_mask=mask)
+        fn = getattr(ta, kind)
+
+        def call(b, fresh=False):
+            if fresh:
+                return fn(b["q"], b["k"], b["v"], **kw)
+            return fn(b["q"], b["k"], b["v"], out=o, lse=lse, **kw)
+    print(f"graph case {i}: {kind}", flush=True)
+    bufs = {k: v.clone() for k, v in xs[0].items()}
     _capture_and_replay(dev, call, bufs, xs[1:] + xs[:1])
