@@ -70,7 +70,11 @@ def _run(ta, dev, d, final=False):
     x, B, C = (to_dev(d[n], dev) for n in ("x", "B", "C"))
     dt, A = to_dev(d["dt"], dev), to_dev(d["A"], dev)
     s0 = to_dev(d["init_state"], dev) if "init_state" in d else None
-    r = ta.ssd_scan(x, dt, A, B, C, init_state=s0, final_state=final)
+    # outputs start as NaN, so an element the kernel does not write fails
+    Bt, L, H, P = x.shape
+    y = torch.full((Bt, L, H, P), float("nan"), dtype=torch.bfloat16, device=dev)
+    fs = torch.full((Bt, H, P, B.shape[3]), float("nan"), dtype=torch.float32, device=dev) if final else False
+    r = ta.ssd_scan(x, dt, A, B, C, init_state=s0, final_state=fs, out=y)
     torch.cuda.synchronize()
     if final:
         return to_np(r[0]), to_np(r[1])
